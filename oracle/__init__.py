@@ -1,0 +1,254 @@
+"""Plain CPU oracle of the LongCat-Flash MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library under ``sparse_moe_layer_02_amd``; each stage here is the
+plain definition written out in C (``moe_oracle.c``, fp64 accumulation, loops
+in index order) and wrapped with ctypes.  The stage functions follow the
+LongCat-Flash Technical Report notes ("Key claims", "Method"; report §2.1,
+§2.2, §2.3.2, §2.4): router over one pool of FFN + zero-computation experts,
+bias for selection only, top-K, identity experts, compensation factor on FFN
+outputs, gate-weighted combine.  The readings taken where the pages are silent
+are stated in ``moe_oracle.c``.
+
+Parity unpinned: whether the score function (softmax), the place where the
+bias enters (the logits), the absence of gate renormalisation and the SwiGLU
+expert form are what LongCat-Flash itself computes -- no page prints the
+router or expert formula.  Everything else is pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c99"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            lib.oracle_router_logits.argtypes = [P, P, I, I, I, P]
+            lib.oracle_router_logits.restype = None
+            lib.oracle_route.argtypes = [P, P, I, I, I, P, P, P]
+            lib.oracle_route.restype = I
+            lib.oracle_gates.argtypes = [P, P, I, I, I, P]
+            lib.oracle_gates.restype = None
+            lib.oracle_permute.argtypes = [P, I, I, I, P, P, P]
+            lib.oracle_permute.restype = I
+            lib.oracle_ffn_row.argtypes = [P, P, P, I, I, P]
+            lib.oracle_ffn_row.restype = None
+            lib.oracle_zero_experts.argtypes = [P, P, P, I, I, I, I, P]
+            lib.oracle_zero_experts.restype = None
+            lib.oracle_combine.argtypes = [P, P, P, P, ctypes.c_double, P, I, I, I, I, P]
+            lib.oracle_combine.restype = None
+            _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+# ---------------------------------------------------------------- stages ----
+
+def router_logits(x: np.ndarray, wr: np.ndarray, threads: int = 1) -> np.ndarray:
+    """fp64 logits[t, e] = sum_h x[t, h] * wr[e, h] (x: [T, H], wr: [E, H])."""
+    lib = _load()
+    x = _c(x, np.float32)
+    wr = _c(wr, np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    out = np.empty((T, E), np.float64)
+    if threads <= 1 or T < 2 * threads:
+        lib.oracle_router_logits(_p(x), _p(wr), T, H, E, _p(out))
+        return out
+    # independent rows; each call is the same single-threaded loop
+    bounds = np.linspace(0, T, threads + 1).astype(int)
+
+    def run(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b > a:
+            lib.oracle_router_logits(_p(x[a:b]), _p(wr), b - a, H, E, _p(out[a:b]))
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(run, range(threads)))
+    return out
+
+
+def route(logits32: np.ndarray, bias: np.ndarray, K: int):
+    """Top-K on fp32 keys = logits32 + bias (ties -> lower expert id).
+
+    Returns (idx int32 [T, K], gate fp64 [T, K], counts int32 [E]).
+    Raises OracleError if a key is NaN."""
+    lib = _load()
+    l = _c(logits32, np.float32)
+    b = _c(bias, np.float32)
+    T, E = l.shape
+    if not (1 <= K <= E):
+        raise ValueError("K out of range")
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float64)
+    counts = np.empty(E, np.int32)
+    rc = lib.oracle_route(_p(l), _p(b), T, E, K, _p(idx), _p(gate), _p(counts))
+    if rc != 0:
+        raise OracleError("NaN routing key")
+    return idx, gate, counts
+
+
+def gates(logits32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Softmax of the unbiased fp32 logits read at arbitrary chosen experts."""
+    lib = _load()
+    l = _c(logits32, np.float32)
+    idx = _c(idx, np.int32)
+    T, E = l.shape
+    K = idx.shape[1]
+    out = np.empty((T, K), np.float64)
+    lib.oracle_gates(_p(l), _p(idx), T, E, K, _p(out))
+    return out
+
+
+def permute(idx: np.ndarray, n_ffn: int):
+    """Returns (offsets [N+1], row_src [S], slot_row [T*K]) -- all int32."""
+    lib = _load()
+    idx = _c(idx, np.int32)
+    T, K = idx.shape
+    offsets = np.empty(n_ffn + 1, np.int32)
+    row_src = np.empty(T * K, np.int32)
+    slot_row = np.empty(T * K, np.int32)
+    S = lib.oracle_permute(_p(idx), T, K, n_ffn, _p(offsets), _p(row_src), _p(slot_row))
+    return offsets, row_src[:S].copy(), slot_row
+
+
+def ffn_row(x: np.ndarray, w13e: np.ndarray, w2e: np.ndarray) -> np.ndarray:
+    """One row through one SwiGLU expert: w2e @ (silu(w13e[:I] x) * (w13e[I:] x))."""
+    lib = _load()
+    x = _c(x, np.float32)
+    w13e = _c(w13e, np.float32)
+    w2e = _c(w2e, np.float32)
+    H = x.shape[0]
+    I = w2e.shape[1]
+    assert w13e.shape == (2 * I, H) and w2e.shape == (H, I)
+    out = np.empty(H, np.float64)
+    lib.oracle_ffn_row(_p(x), _p(w13e), _p(w2e), H, I, _p(out))
+    return out
+
+
+def ffn_rows(x_rows: np.ndarray, w13e: np.ndarray, w2e: np.ndarray, threads: int = 1) -> np.ndarray:
+    """Several rows through the same expert (rows are independent)."""
+    lib = _load()
+    x_rows = _c(x_rows, np.float32)
+    w13e = _c(w13e, np.float32)
+    w2e = _c(w2e, np.float32)
+    R, H = x_rows.shape
+    I = w2e.shape[1]
+    out = np.empty((R, H), np.float64)
+
+    def run(r):
+        lib.oracle_ffn_row(_p(x_rows[r]), _p(w13e), _p(w2e), H, I, _p(out[r]))
+
+    if threads <= 1 or R == 1:
+        for r in range(R):
+            run(r)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, range(R)))
+    return out
+
+
+def expert_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13: np.ndarray, w2: np.ndarray,
+               threads: int = 1) -> np.ndarray:
+    """Every grouped row through its expert.  x_perm [S, H]; w13 [N, 2I, H]; w2 [N, H, I]."""
+    S, H = x_perm.shape
+    out = np.empty((S, H), np.float64)
+    N = w13.shape[0]
+    for e in range(N):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            out[a:b] = ffn_rows(x_perm[a:b], w13[e], w2[e], threads=threads)
+    return out
+
+
+def zero_experts(x: np.ndarray, idx: np.ndarray, gate: np.ndarray, n_ffn: int) -> np.ndarray:
+    """y_acc[t] = (sum of gates of the identity experts t chose) * x[t]."""
+    lib = _load()
+    x = _c(x, np.float32)
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float64)
+    T, H = x.shape
+    K = idx.shape[1]
+    out = np.empty((T, H), np.float64)
+    lib.oracle_zero_experts(_p(x), _p(idx), _p(gate), T, H, K, n_ffn, _p(out))
+    return out
+
+
+def combine(y_perm: np.ndarray, slot_row: np.ndarray, idx: np.ndarray, gate: np.ndarray,
+            scale: float, y_acc: np.ndarray, n_ffn: int) -> np.ndarray:
+    """y[t] = y_acc[t] + sum over FFN slots of scale * gate * y_perm[row]."""
+    lib = _load()
+    y_perm = _c(y_perm, np.float64)
+    slot_row = _c(slot_row, np.int32)
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float64)
+    y_acc = _c(y_acc, np.float64)
+    T, H = y_acc.shape
+    K = idx.shape[1]
+    if y_perm.size == 0:
+        y_perm = np.zeros((1, H), np.float64)
+    out = np.empty((T, H), np.float64)
+    lib.oracle_combine(_p(y_perm), _p(slot_row), _p(idx), _p(gate), float(scale), _p(y_acc),
+                       T, H, K, n_ffn, _p(out))
+    return out
+
+
+# ------------------------------------------------------------ whole layer ----
+
+def layer(x, wr, bias, w13, w2, K: int, scale: float, threads: int = 1) -> dict:
+    """The forward pass composed from the stages, in the order the layer runs
+    them: scores -> top-K -> dispatch -> FFN experts -> identity experts ->
+    combine.  All arrays are numpy fp32 (bf16 values are exact in fp32)."""
+    x = _c(x, np.float32)
+    N = w13.shape[0]
+    logits = router_logits(x, wr, threads=threads)
+    logits32 = logits.astype(np.float32)
+    idx, gate, counts = route(logits32, bias, K)
+    offsets, row_src, slot_row = permute(idx, N)
+    x_perm = x[row_src // K] if row_src.size else np.zeros((0, x.shape[1]), np.float32)
+    y_perm = expert_ffn(x_perm, offsets, w13, w2, threads=threads)
+    y_acc = zero_experts(x, idx, gate, N)
+    y = combine(y_perm, slot_row, idx, gate, scale, y_acc, N)
+    return dict(logits=logits, logits32=logits32, idx=idx, gate=gate, counts=counts,
+                offsets=offsets, row_src=row_src, slot_row=slot_row, x_perm=x_perm,
+                y_perm=y_perm, y_acc=y_acc, y=y)
