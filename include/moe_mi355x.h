@@ -1,0 +1,147 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) forward pass of a LongCat-Flash
+ * Mixture-of-Experts layer: a pool of N SwiGLU FFN experts plus Z
+ * zero-computation (identity) experts, a per-expert selection bias, top-K
+ * routing, expert-grouped FFN GEMMs, identity passthrough and a compensated,
+ * gate-weighted combine.
+ *
+ * Source of the method: LongCat-Flash Technical Report notes, "Key claims"
+ * and "Method" (report §2.1 zero-computation experts and the PID-adjusted
+ * expert bias, §2.2 dispatch/combine, §2.3.2 Eq. 8 variance compensation,
+ * §2.4 model configuration: K = 12 of 512 FFN + 256 zero experts, hidden
+ * 6144, expert intermediate 2048).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is DEVICE memory owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream) and returns without synchronising.
+ *     Calls on one stream may follow each other with no host round trip:
+ *     data-dependent sizes (rows per expert) stay on the device.
+ *   - Arguments are validated on the host BEFORE any HIP call; a failed check
+ *     returns a status and enqueues nothing.  A launch failure returns
+ *     MOE_ERR_LAUNCH.  No call aborts the process.
+ *   - Layouts are row-major.  Expert ids: FFN experts 0..n_ffn-1, identity
+ *     experts n_ffn..E-1.  Routing tensors (logits, bias, gates, y_acc) are
+ *     fp32, index tensors int32.  Activations, expert weights and the layer
+ *     output share one dtype: MOE_F32 or MOE_BF16 (fp32 accumulation always).
+ *   - Pointers to bf16 data must be 16-byte aligned, other pointers 4-byte
+ *     aligned (MOE_ERR_ALIGN).  T*K must stay below 2^31.
+ *   - Results are bitwise deterministic run to run (no floating-point
+ *     atomics), the property the report's SDC detection relies on (report §1,
+ *     §3.1.3).
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,     /* a size is out of range or not a supported multiple */
+    MOE_ERR_DTYPE = 3,     /* unknown dtype */
+    MOE_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+    MOE_ERR_WORKSPACE = 5, /* workspace smaller than the *_workspace_bytes query */
+    MOE_ERR_LAUNCH = 6     /* a HIP launch failed (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Router scores of every expert of the pool (Technical Report notes, Key
+ * claims [§2.1, §2.4]: the router picks from one pool of FFN + zero experts).
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h], fp32 result.
+ * x: [T][H] in x_dtype; w_router: [E][H] fp32; logits: [T][E] fp32.
+ * Any T, E >= 1; H >= 1 (H % 64 == 0 for MOE_BF16, which runs on bf16 matrix
+ * cores with w_router split exactly into three bf16 parts). */
+moe_status moe_router_logits(const void *x, int x_dtype, const float *w_router,
+                             int T, int H, int E, float *logits, void *stream);
+
+/* Top-K routing with a selection bias (Technical Report notes, Key claims
+ * [§2.1.1]: the bias the PID controller adjusts from routing frequency enters
+ * selection only).
+ *   key[t][e] = logits[t][e] + bias[e]         (one fp32 addition)
+ *   topk_idx[t][k]: the K largest keys, in descending key order; equal keys go
+ *     to the lower expert id (-0.0 equals +0.0; -inf is a valid key, i.e. a
+ *     masked expert; a NaN key ranks below -inf).
+ *   topk_gate[t][k] = softmax over all E unbiased logits, taken at the chosen
+ *     expert; not renormalised over the K picks.
+ *   counts[e] = number of tokens that chose e (the routing-frequency
+ *     histogram), overwritten (not accumulated).
+ *   dev_status (may be NULL): an int32 the kernels set to 1 when a key is NaN
+ *     or a logit is not finite; they never clear it -- the caller zeroes it.
+ * logits [T][E], bias [E], topk_idx/topk_gate [T][K], counts [E].
+ * 1 <= K <= E <= 1024, T >= 1. */
+moe_status moe_route(const float *logits, const float *bias, int T, int E, int K,
+                     int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                     int32_t *dev_status, void *stream);
+
+/* Dispatch on one GPU: group every FFN selection by expert (Technical Report
+ * notes, Key claims [§2.2], the dispatch half of dispatch/combine).
+ * Rows are expert-major and, within an expert, in ascending token order.
+ *   offsets[e] = first row of expert e, offsets[n_ffn] = S (FFN rows)
+ *   x_perm[r] = x[t] for the selection (t, k) held by row r, r < S
+ *   row_src[r] = t*K + k, r < S
+ *   slot_row[t*K + k] = its row, or -1 when it chose an identity expert
+ * x: [T][H] (dtype); topk_idx: [T][K] with entries in [0, E); x_perm: capacity
+ * [T*K][H]; row_src: capacity [T*K]; slot_row: [T*K]; offsets: [n_ffn + 1].
+ * Rows >= S of x_perm and row_src are left untouched.
+ * ws: device workspace of at least moe_permute_workspace_bytes(T, K, n_ffn). */
+size_t moe_permute_workspace_bytes(int T, int K, int n_ffn);
+moe_status moe_permute(const void *x, int dtype, const int32_t *topk_idx,
+                       int T, int H, int K, int n_ffn, int32_t *offsets,
+                       void *x_perm, int32_t *row_src, int32_t *slot_row,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* The FFN experts on their grouped rows (Technical Report notes, Key claims
+ * [§2.4]: fine-grained FFN experts of intermediate size I; SwiGLU form).
+ * For every expert e with rows [offsets[e], offsets[e+1]) (empty experts cost
+ * nothing):
+ *   hh = silu(X W_g^T) * (X W_u^T),  silu(a) = a / (1 + exp(-a))
+ *   y_perm rows = hh W_d^T
+ * w13: [n_ffn][2I][H] (rows 0..I-1 = W_g, I..2I-1 = W_u); w2: [n_ffn][H][I];
+ * x_perm, y_perm: [rows_cap][H]; offsets as written by moe_permute, with
+ * offsets[n_ffn] <= rows_cap.  Only rows < offsets[n_ffn] of y_perm are
+ * written.  fp32 accumulation; for MOE_BF16, hh is rounded to bf16 between
+ * the two GEMMs and y_perm is stored in bf16.
+ * MOE_BF16 requires H % 128 == 0 and I % 64 == 0.
+ * ws: at least moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype). */
+size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype);
+moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, int rows_cap,
+                          int n_ffn, int H, int I, const void *w13, const void *w2,
+                          int dtype, void *y_perm, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Zero-computation experts (Technical Report notes, Key claims [§2.1]:
+ * identity experts return their input):
+ *   y_acc[t][h] = (sum over slots k with topk_idx >= n_ffn of topk_gate[t][k]) * x[t][h]
+ * x: [T][H] (dtype); topk_idx, topk_gate: [T][K]; y_acc: [T][H] fp32. */
+moe_status moe_zero_experts(const void *x, int dtype, const int32_t *topk_idx,
+                            const float *topk_gate, int T, int H, int K, int n_ffn,
+                            float *y_acc, void *stream);
+
+/* Combine (Technical Report notes, Key claims [§2.2] the combine half;
+ * [§2.3.2 Eq. 8] the variance-compensation factor on FFN expert outputs):
+ *   y[t] = y_acc[t] + sum over slots k with slot_row >= 0, in slot order, of
+ *          (ffn_scale * topk_gate[t][k]) * y_perm[slot_row[t*K + k]]
+ * accumulated in fp32, then stored in dtype (bf16: round to nearest even).
+ * y_perm: rows as written by moe_expert_ffn; slot_row as written by
+ * moe_permute; y_acc from moe_zero_experts; y: [T][H] (dtype). */
+moe_status moe_combine(const void *y_perm, int dtype, const int32_t *slot_row,
+                       const float *topk_gate, float ffn_scale, const float *y_acc,
+                       int T, int H, int K, void *y, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

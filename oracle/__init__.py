@@ -252,3 +252,20 @@ def layer(x, wr, bias, w13, w2, K: int, scale: float, threads: int = 1) -> dict:
     return dict(logits=logits, logits32=logits32, idx=idx, gate=gate, counts=counts,
                 offsets=offsets, row_src=row_src, slot_row=slot_row, x_perm=x_perm,
                 y_perm=y_perm, y_acc=y_acc, y=y)
+
+
+def layer_with_routing(x, logits32, idx, w13, w2, scale: float, threads: int = 1) -> np.ndarray:
+    """The layer output for a given choice of experts idx [T, K]: gates are
+    the oracle's softmax of logits32 at those experts; dispatch, experts,
+    identity experts and combine as in ``layer``.  Used where a token's top-K
+    set is decided by a near-tie (the chosen set, not the arithmetic, differs)."""
+    x = _c(x, np.float32)
+    idx = _c(idx, np.int32)
+    K = idx.shape[1]
+    N = w13.shape[0]
+    gate = gates(logits32, idx)
+    offsets, row_src, slot_row = permute(idx, N)
+    x_perm = x[row_src // K] if row_src.size else np.zeros((0, x.shape[1]), np.float32)
+    y_perm = expert_ffn(x_perm, offsets, w13, w2, threads=threads)
+    y_acc = zero_experts(x, idx, gate, N)
+    return combine(y_perm, slot_row, idx, gate, scale, y_acc, N)

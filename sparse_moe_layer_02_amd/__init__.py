@@ -1,0 +1,222 @@
+"""Python binding of the MI355X MoE-layer library (``include/moe_mi355x.h``).
+
+Argument marshalling only: each function below has the name of the C entry
+point it calls, checks dtypes/devices/shapes of the torch tensors it is given,
+and passes their device pointers plus the current HIP stream.  Every step of
+the layer runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback -- if the shared library is missing, importing a function raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "moe_router_logits": ([_P, _I, _P, _I, _I, _I, _P, _P], _I),
+    "moe_route": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
+    "moe_permute_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "moe_permute": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "moe_expert_ffn_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "moe_expert_ffn": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
+    "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
+    "moe_status_string": ([_I], ctypes.c_char_p),
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {lib().moe_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded shared library (raises if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                                   "(python -c 'import __graft_entry__ as g; g.build()')")
+            l = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGS.items():
+                f = getattr(l, name)
+                f.argtypes = args
+                f.restype = res
+            _lib = l
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def _dev(*ts):
+    d = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if d is None:
+            d = t.device
+        elif t.device != d:
+            raise ValueError("tensors on different devices")
+    return d
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+# --------------------------------------------------------------- the calls --
+
+def moe_router_logits(x, w_router, logits):
+    """logits[T, E] (fp32) = x[T, H] @ w_router[E, H]^T."""
+    _dev(x, w_router, logits)
+    _want(w_router, torch.float32, "w_router")
+    _want(logits, torch.float32, "logits")
+    T, H = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape == (E, H) and logits.shape == (T, E)
+    _check("moe_router_logits", lib().moe_router_logits(
+        _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
+
+
+def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
+    """Top-K of logits + bias (lower id on ties), softmax gates, histogram."""
+    _dev(logits, bias, topk_idx, topk_gate, counts, dev_status)
+    T, E = logits.shape
+    _want(logits, torch.float32, "logits")
+    _want(bias, torch.float32, "bias")
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_gate, torch.float32, "topk_gate")
+    _want(counts, torch.int32, "counts")
+    assert bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K)
+    assert counts.shape == (E,)
+    _check("moe_route", lib().moe_route(
+        _ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+        _ptr(dev_status), _stream(logits)))
+
+
+def moe_permute_workspace_bytes(T, K, n_ffn):
+    return int(lib().moe_permute_workspace_bytes(T, K, n_ffn))
+
+
+def moe_permute(x, topk_idx, n_ffn, offsets, x_perm, row_src, slot_row, ws):
+    """Expert-major, token-ascending grouping of the FFN selections."""
+    _dev(x, topk_idx, offsets, x_perm, row_src, slot_row, ws)
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    assert x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K
+    _check("moe_permute", lib().moe_permute(
+        _ptr(x), _DT[x.dtype], _ptr(topk_idx), T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm),
+        _ptr(row_src), _ptr(slot_row), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+
+
+def moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype):
+    return int(lib().moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, _DT[dtype]))
+
+
+def moe_expert_ffn(x_perm, offsets, w13, w2, y_perm, ws):
+    """SwiGLU experts on the grouped rows; empty experts skipped."""
+    _dev(x_perm, offsets, w13, w2, y_perm, ws)
+    rows_cap, H = x_perm.shape
+    N, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape == x_perm.shape
+    assert w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _ptr(x_perm), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2), _DT[x_perm.dtype],
+        _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x_perm)))
+
+
+def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
+    """y_acc = (sum of identity-expert gates) * x, fp32."""
+    _dev(x, topk_idx, topk_gate, y_acc)
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    _want(y_acc, torch.float32, "y_acc")
+    _check("moe_zero_experts", lib().moe_zero_experts(
+        _ptr(x), _DT[x.dtype], _ptr(topk_idx), _ptr(topk_gate), T, H, K, n_ffn, _ptr(y_acc),
+        _stream(x)))
+
+
+def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
+    """y = y_acc + sum of ffn_scale * gate * y_perm rows, in slot order."""
+    _dev(y_perm, slot_row, topk_gate, y_acc, y)
+    T, H = y.shape
+    K = topk_gate.shape[1]
+    assert y_perm.dtype == y.dtype
+    _check("moe_combine", lib().moe_combine(
+        _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
+        _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
+
+
+# ------------------------------------------------------- buffers + forward --
+
+def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda"):
+    """Device buffers for one forward pass (torch allocations; no compute)."""
+    rows = T * K
+    f32, i32 = torch.float32, torch.int32
+    return dict(
+        logits=torch.empty((T, E), dtype=f32, device=device),
+        topk_idx=torch.empty((T, K), dtype=i32, device=device),
+        topk_gate=torch.empty((T, K), dtype=f32, device=device),
+        counts=torch.empty((E,), dtype=i32, device=device),
+        status=torch.zeros((1,), dtype=i32, device=device),
+        offsets=torch.empty((n_ffn + 1,), dtype=i32, device=device),
+        x_perm=torch.empty((rows, H), dtype=dtype, device=device),
+        row_src=torch.empty((rows,), dtype=i32, device=device),
+        slot_row=torch.empty((rows,), dtype=i32, device=device),
+        ws_perm=torch.empty((max(16, moe_permute_workspace_bytes(T, K, n_ffn)),),
+                            dtype=torch.uint8, device=device),
+        y_perm=torch.empty((rows, H), dtype=dtype, device=device),
+        ws_ffn=torch.empty((max(256, moe_expert_ffn_workspace_bytes(rows, n_ffn, I, dtype)),),
+                           dtype=torch.uint8, device=device),
+        y_acc=torch.empty((T, H), dtype=f32, device=device),
+        y=torch.empty((T, H), dtype=dtype, device=device),
+    )
+
+
+def forward(x, w_router, bias, w13, w2, K, ffn_scale, buf):
+    """The six calls of one layer forward, enqueued back to back on the
+    current stream (no host synchronisation)."""
+    n_ffn = w13.shape[0]
+    moe_router_logits(x, w_router, buf["logits"])
+    moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
+              buf["status"])
+    moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], buf["x_perm"], buf["row_src"],
+                buf["slot_row"], buf["ws_perm"])
+    moe_expert_ffn(buf["x_perm"], buf["offsets"], w13, w2, buf["y_perm"], buf["ws_ffn"])
+    moe_zero_experts(x, buf["topk_idx"], buf["topk_gate"], n_ffn, buf["y_acc"])
+    moe_combine(buf["y_perm"], buf["slot_row"], buf["topk_gate"], ffn_scale, buf["y_acc"],
+                buf["y"])
+    return buf["y"]

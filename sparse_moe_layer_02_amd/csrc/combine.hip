@@ -1,0 +1,129 @@
+// Identity experts and the combine step (LongCat-Flash Technical Report notes,
+// Key claims [§2.1] identity "zero-computation" experts, [§2.2] combine,
+// [§2.3.2 Eq. 8] the variance-compensation factor on FFN expert outputs).
+// Both are HBM-bound row sweeps: one block per token, 16-byte vector loads,
+// 8 elements per thread-step, fp32 arithmetic, a fixed summation order (slot
+// order) and no atomics, so results are bitwise reproducible.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 1024;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float* o) {
+    bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float* o) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)o[i];
+    *(bf16x8*)p = v;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* o) {
+    f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* o) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = o[i]; b[i] = o[4 + i]; }
+    *(f32x4*)p = a;
+    *(f32x4*)(p + 4) = b;
+  }
+};
+
+// y_acc[t] = (sum of the gates of t's identity-expert slots) * x[t]
+template <typename T>
+__global__ __launch_bounds__(kThreads) void zero_experts_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    int H, int K, int n_ffn, float* __restrict__ y_acc) {
+  const int t = blockIdx.x;
+  float gs = 0.0f;
+  for (int k = 0; k < K; ++k)
+    if (idx[(size_t)t * K + k] >= n_ffn) gs += gate[(size_t)t * K + k];
+  const T* xr = x + (size_t)t * H;
+  float* yr = y_acc + (size_t)t * H;
+  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    float v[8];
+    Vec8<T>::load(xr + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= gs;
+    Vec8<float>::store(yr + c, v);
+  }
+}
+
+// y[t] = y_acc[t] + sum over FFN slots (in slot order) of (scale*gate) * y_perm[row]
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const T* __restrict__ y_perm, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ gate, float scale, const float* __restrict__ y_acc, int H, int K,
+    T* __restrict__ y) {
+  __shared__ int rows[kMaxK];
+  __shared__ float wts[kMaxK];
+  __shared__ int nrows;
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int k = 0; k < K; ++k) {
+      int r = slot_row[(size_t)t * K + k];
+      if (r >= 0) {
+        rows[n] = r;
+        wts[n] = scale * gate[(size_t)t * K + k];
+        ++n;
+      }
+    }
+    nrows = n;
+  }
+  __syncthreads();
+  const int n = nrows;
+  const float* ar = y_acc + (size_t)t * H;
+  T* yr = y + (size_t)t * H;
+  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    float acc[8];
+    Vec8<float>::load(ar + c, acc);
+    for (int j = 0; j < n; ++j) {
+      float v[8];
+      Vec8<T>::load(y_perm + (size_t)rows[j] * H + c, v);
+      const float w = wts[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+    Vec8<T>::store(yr + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, const float* gate,
+                               int T, int H, int K, int n_ffn, float* y_acc, hipStream_t s) {
+  if (dtype == MOE_BF16)
+    zero_experts_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)x, idx, gate, H, K, n_ffn,
+                                                     y_acc);
+  else
+    zero_experts_kernel<float><<<T, kThreads, 0, s>>>((const float*)x, idx, gate, H, K, n_ffn,
+                                                      y_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row,
+                          const float* gate, float scale, const float* y_acc, int T, int H,
+                          int K, void* y, hipStream_t s) {
+  if (dtype == MOE_BF16)
+    combine_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)y_perm, slot_row, gate, scale,
+                                                y_acc, H, K, (bf16*)y);
+  else
+    combine_kernel<float><<<T, kThreads, 0, s>>>((const float*)y_perm, slot_row, gate, scale,
+                                                 y_acc, H, K, (float*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

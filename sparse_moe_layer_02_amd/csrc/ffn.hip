@@ -1,0 +1,331 @@
+// FFN experts on expert-grouped rows (LongCat-Flash Technical Report notes,
+// Key claims [§2.4]: fine-grained FFN experts, intermediate 2048 at hidden
+// 6144; SwiGLU form):
+//   hh = silu(X W_g^T) * (X W_u^T),  Y = hh W_d^T,  per expert, empty experts skipped.
+//
+// Work list.  A small kernel turns offsets[] into m-tiles (expert, first row,
+// rows <= BM); the GEMM grids are sized on the host from the capacity bound
+// (rows_cap / BM + n_ffn m-tiles) and blocks past the real count exit.
+//
+// bf16 path (gfx950 matrix cores, v_mfma_f32_16x16x32_bf16, fp32 accumulate):
+//   - one block = one m-tile (all of the expert's rows, up to BM) x 128 rows
+//     of the weight matrix, so every weight tile is fetched from HBM once when
+//     an expert's rows fit one m-tile -- the regime of the full-scale layer,
+//     where the weights (not the MFMA rate) bound the time;
+//   - K is swept in 64-element stages (128 B per row) held in LDS; stages are
+//     filled by global_load_lds_dwordx4 (16 B per lane straight into LDS, no
+//     VGPR staging) and several stages are in flight;
+//   - LDS rows are 128 B with the 16-byte chunks XOR-swizzled by
+//     (row ^ row>>3) & 7, which keeps the ds_read_b128 fragment reads free of
+//     bank conflicts for both 8- and 16-lane phases;
+//   - wave w owns 32 weight rows (two 16-column MFMA blocks) and every row
+//     block of the m-tile; 16-row blocks past the expert's rows are skipped;
+//   - gate/up: weight rows are paired so that a lane holds gate column j and
+//     up column j in the same accumulator slot, and silu(g)*u is applied in
+//     registers before hh is stored (bf16);
+//   - block -> tile order is XCD-aware: consecutive blocks land on the 8 XCDs
+//     in turn, so all column tiles of one m-tile run on one XCD and re-read
+//     the m-tile's activation rows from that XCD's L2.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;      // k elements per stage: 128 B per LDS row
+constexpr int kBN = 128;     // weight rows per block
+constexpr int kRowBytes = kBK * 2;
+constexpr int kBmBf16 = 256;
+constexpr int kStagesBf16 = 3;
+constexpr int kBmF32 = 32;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
+
+// ------------------------------------------------------------ work list --
+// Rows are clamped to [0, rows_cap) and the list to max_tiles entries, so a
+// malformed offsets[] can shrink the work but never index past the buffers.
+__global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ offsets, int n_ffn,
+                                                  int bm, int rows_cap, int max_tiles,
+                                                  int4* __restrict__ tiles,
+                                                  int* __restrict__ ntiles) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_ffn + 1023) / 1024;
+  const int lo = min(n_ffn, tid * per), hi = min(n_ffn, lo + per);
+  auto span = [&](int e, int& r0, int& m) {
+    r0 = min(max(offsets[e], 0), rows_cap);
+    m = min(max(offsets[e + 1], r0), rows_cap) - r0;
+  };
+  int s = 0;
+  for (int e = lo; e < hi; ++e) {
+    int r0, m;
+    span(e, r0, m);
+    s += (m + bm - 1) / bm;
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int pos = part[tid] - s;
+  for (int e = lo; e < hi; ++e) {
+    int r0, m;
+    span(e, r0, m);
+    for (int j = 0; j * bm < m && pos < max_tiles; ++j)
+      tiles[pos++] = make_int4(e, r0 + j * bm, min(bm, m - j * bm), 0);
+  }
+  if (tid == 1023) *ntiles = min(part[1023], max_tiles);
+}
+
+// -------------------------------------------------------- bf16 MFMA GEMM --
+// GATEUP: A = x_perm [.][H], W = w13 [N][2I][H], C = hh [.][I]   (KD = H, NT = I/64)
+// down  : A = hh     [.][I], W = w2  [N][H][I],  C = y_perm [.][H] (KD = I, NT = H/128)
+//
+// The K loop is instantiated per number G of live 32-row groups of the m-tile
+// (G = ceil(rows / 32)), chosen once per block: each instance is branch-free,
+// loads only the live A rows and issues only the live MFMAs, so the compiler
+// can overlap fragment reads with matrix-core work.
+template <int BM, int STAGES>
+struct Smem {
+  static constexpr int kStageBytes = (BM + kBN) * kRowBytes;
+  static constexpr int kBytes = STAGES * kStageBytes;
+};
+
+template <int G, int BM, int STAGES>
+__device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_src,
+                                             const bf16* const* b_src, int KD, int wave, int lane,
+                                             f32x4 (&acc)[BM / 16][2]) {
+  constexpr int kStageBytes = Smem<BM, STAGES>::kStageBytes;
+  constexpr int kAq = G;        // A load instructions per wave: 4 waves x 8 rows x G = 32G rows
+  constexpr int kLoads = kAq + kBN / 32;       // load instructions per wave per stage
+  const int KT = KD / kBK;
+  auto issue = [&](int stage, int k0) {
+    char* sb = smem + stage * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < kAq; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kBN / 32; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
+                                       (lds_void*)(sb + BM * kRowBytes + (wave + 4 * q) * 1024),
+                                       16, 0, 0);
+  };
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s * kBK);
+
+  const int rB0 = 32 * wave + (lane & 15);
+  const int rB1 = rB0 + 16;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + STAGES - 1 <= KT) wait_vmcnt<kLoads * (STAGES - 2)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * kBK);
+    const char* As = smem + (kt % STAGES) * kStageBytes;
+    const char* Bs = As + BM * kRowBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      const bf16x8 b0 = *(const bf16x8*)(Bs + rB0 * kRowBytes + swz(rB0, ch) * 16);
+      const bf16x8 b1 = *(const bf16x8*)(Bs + rB1 * kRowBytes + swz(rB1, ch) * 16);
+      bf16x8 a[2 * G];
+#pragma unroll
+      for (int rb = 0; rb < 2 * G; ++rb) {
+        const int rA = rb * 16 + (lane & 15);
+        a[rb] = *(const bf16x8*)(As + rA * kRowBytes + swz(rA, ch) * 16);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2 * G; ++rb) {
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b0, acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b1, acc[rb][1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int BM, int STAGES, bool GATEUP>
+__global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const int4* __restrict__ tiles,
+    const int* __restrict__ ntiles, int KD, int I, int H, int NT, bf16* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char smem[Smem<BM, STAGES>::kBytes];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NT) * 8 + xcd;
+  const int nt = slot % NT;
+  if (mt >= *ntiles) return;
+  const int4 tile = tiles[mt];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int lr = lane >> 3;      // row within an 8-row load group
+  const int lc = lane & 7;       // 16-byte slot within the LDS row
+
+  // global source of this lane's 16-byte loads (k offset added per stage);
+  // rows past the tile are clamped to its last row (never used)
+  const bf16* a_src[BM / 32];
+#pragma unroll
+  for (int q = 0; q < BM / 32; ++q) {
+    const int r = (wave + 4 * q) * 8 + lr;
+    a_src[q] = A + (size_t)(row0 + min(r, rows - 1)) * KD + swz(r, lc) * 8;
+  }
+  const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
+  const bf16* wexp = W + (size_t)e * wrows * KD;
+  const bf16* b_src[kBN / 32];
+#pragma unroll
+  for (int q = 0; q < kBN / 32; ++q) {
+    const int r = (wave + 4 * q) * 8 + lr;
+    int wr;
+    if (GATEUP) {
+      const int j = nt * 64 + 16 * (r >> 5) + (r & 15);
+      wr = (r & 16) ? I + j : j;
+    } else {
+      wr = nt * kBN + r;
+    }
+    b_src[q] = wexp + (size_t)wr * KD + swz(r, lc) * 8;
+  }
+
+  f32x4 acc[BM / 16][2];
+#pragma unroll
+  for (int i = 0; i < BM / 16; ++i) {
+    acc[i][0] = f32x4{0, 0, 0, 0};
+    acc[i][1] = f32x4{0, 0, 0, 0};
+  }
+  const int groups = (rows + 31) >> 5;
+  switch (groups) {
+#define MOE_CASE(g) \
+    case g: ffn_mainloop<g, BM, STAGES>(smem, a_src, b_src, KD, wave, lane, acc); break;
+    MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
+    MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+#undef MOE_CASE
+    default: break;
+  }
+  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
+
+  // epilogue: lane holds C[16*rb + 4*(lane>>4) + i][col (lane & 15)] of both blocks
+#pragma unroll
+  for (int rb = 0; rb < BM / 16; ++rb) {
+    if (rb * 16 >= rows) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + 4 * (lane >> 4) + i;
+      if (r >= rows) continue;
+      if (GATEUP) {
+        const float g = acc[rb][0][i], u = acc[rb][1][i];
+        const float hv = g / (1.0f + expf(-g)) * u;
+        C[(size_t)(row0 + r) * I + nt * 64 + 16 * wave + (lane & 15)] = (bf16)hv;
+      } else {
+        bf16* crow = C + (size_t)(row0 + r) * H + nt * kBN + 32 * wave + (lane & 15);
+        crow[0] = (bf16)acc[rb][0][i];
+        crow[16] = (bf16)acc[rb][1][i];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ fp32 path --
+// Plain LDS-tiled FMA kernels for fp32 layers (exact fp32 products, fp32
+// accumulation); any H and I.  Tile: 32 rows x 32 outputs, K step 32.
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void ffn_f32(const float* __restrict__ A,
+                                                    const float* __restrict__ W,
+                                                    const int4* __restrict__ tiles,
+                                                    const int* __restrict__ ntiles, int KD, int I,
+                                                    int H, float* __restrict__ C) {
+  constexpr int TM = 32, TN = 32, TK = 32;
+  constexpr int NB = GATEUP ? 2 * TN : TN;   // weight rows per tile
+  __shared__ float As[TK][TM + 1];
+  __shared__ float Bs[TK][NB + 1];
+  const int mt = blockIdx.y;
+  if (mt >= *ntiles) return;
+  const int4 tile = tiles[mt];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const int n0 = blockIdx.x * TN;
+  const int NOUT = GATEUP ? I : H;
+  const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
+  const float* wexp = W + (size_t)e * wrows * KD;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // outputs: rows ty*2+{0,1}, cols tx*2+{0,1}
+  float acc[2][2][2] = {};
+  for (int k0 = 0; k0 < KD; k0 += TK) {
+    for (int i = threadIdx.x; i < TM * TK; i += kThreads) {
+      const int r = i / TK, k = i % TK;
+      As[k][r] = (r < rows && k0 + k < KD) ? A[(size_t)(row0 + r) * KD + k0 + k] : 0.0f;
+    }
+    for (int i = threadIdx.x; i < NB * TK; i += kThreads) {
+      const int c = i / TK, k = i % TK;
+      int n = n0 + (c % TN);
+      int wr = (GATEUP && c >= TN) ? I + n : n;
+      Bs[k][c] = (n < NOUT && k0 + k < KD) ? wexp[(size_t)wr * KD + k0 + k] : 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < TK; ++k) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float a = As[k][ty * 2 + i];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j][0] = fmaf(a, Bs[k][tx * 2 + j], acc[i][j][0]);
+          if (GATEUP) acc[i][j][1] = fmaf(a, Bs[k][TN + tx * 2 + j], acc[i][j][1]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = ty * 2 + i, n = n0 + tx * 2 + j;
+      if (r >= rows || n >= NOUT) continue;
+      float v = acc[i][j][0];
+      if (GATEUP) v = v / (1.0f + expf(-v)) * acc[i][j][1];
+      C[(size_t)(row0 + r) * NOUT + n] = v;
+    }
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline int ffn_bm(int dtype) { return dtype == MOE_BF16 ? kBmBf16 : kBmF32; }
+inline size_t max_mtiles(int rows_cap, int n_ffn, int bm) { return (size_t)rows_cap / bm + n_ffn + 8; }
+
+}  // namespace
+
+size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype) {
+  const int es = dtype == MOE_BF16 ? 2 : 4;
+  return 256 + align256(max_mtiles(rows_cap, n_ffn, ffn_bm(dtype)) * sizeof(int4)) +
+         align256((size_t)rows_cap * I * es);
+}
+
+hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
+                             int H, int I, const void* w13, const void* w2, int dtype,
+                             void* y_perm, void* ws, hipStream_t s) {
+  const int bm = ffn_bm(dtype);
+  const size_t mtmax = max_mtiles(rows_cap, n_ffn, bm);
+  int* ntiles = (int*)ws;
+  int4* tiles = (int4*)((char*)ws + 256);
+  void* hh = (char*)ws + 256 + align256(mtmax * sizeof(int4));
+  ffn_tiles<<<1, 1024, 0, s>>>(offsets, n_ffn, bm, rows_cap, (int)mtmax, tiles, ntiles);
+  if (dtype == MOE_BF16) {
+    const unsigned groups = ceil_div(mtmax, 8);
+    const int nt1 = I / 64, nt2 = H / kBN;
+    ffn_mfma_bf16<kBmBf16, kStagesBf16, true><<<groups * 8 * nt1, kThreads, 0, s>>>(
+        (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1, (bf16*)hh);
+    ffn_mfma_bf16<kBmBf16, kStagesBf16, false><<<groups * 8 * nt2, kThreads, 0, s>>>(
+        (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2, (bf16*)y_perm);
+  } else {
+    dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
+    ffn_f32<true><<<g1, kThreads, 0, s>>>((const float*)x_perm, (const float*)w13, tiles, ntiles,
+                                          H, I, H, (float*)hh);
+    ffn_f32<false><<<g2, kThreads, 0, s>>>((const float*)hh, (const float*)w2, tiles, ntiles, I,
+                                           I, H, (float*)y_perm);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

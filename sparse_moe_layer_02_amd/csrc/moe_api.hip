@@ -1,0 +1,133 @@
+// C-ABI entry points: host-side validation (no HIP call before it passes),
+// then the kernels are enqueued on the caller's stream.  See
+// include/moe_mi355x.h for the contract of each call.
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 1024;      // route: one wave64 holds up to 16 keys per lane
+constexpr int kMaxFfn = 4096;    // permute: 64-bit LDS mask per FFN expert
+constexpr int kMaxKCombine = 1024;
+
+inline bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline bool fits_i32(long long v) { return v >= 0 && v < (1ll << 31); }
+
+inline moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "unsupported shape";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_ALIGN: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_router_logits(const void* x, int x_dtype, const float* w_router, int T, int H,
+                             int E, float* logits, void* stream) {
+  if (!x || !w_router || !logits) return MOE_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || E < 1 || !fits_i32((long long)T * E)) return MOE_ERR_SHAPE;
+  if (!aligned(x, x_dtype == MOE_BF16 ? 2 : 4) || !aligned(w_router, 4) || !aligned(logits, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_router_logits(x, x_dtype, w_router, T, H, E, logits,
+                                       (hipStream_t)stream));
+}
+
+moe_status moe_route(const float* logits, const float* bias, int T, int E, int K,
+                     int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* dev_status,
+                     void* stream) {
+  if (!logits || !bias || !topk_idx || !topk_gate || !counts) return MOE_ERR_NULL;
+  if (T < 1 || E < 1 || E > kMaxE || K < 1 || K > E || !fits_i32((long long)T * K) ||
+      !fits_i32((long long)T * E))
+    return MOE_ERR_SHAPE;
+  if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) ||
+      !aligned(topk_gate, 4) || !aligned(counts, 4) || !aligned(dev_status, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_route(logits, bias, T, E, K, topk_idx, topk_gate, counts, dev_status,
+                               (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_bytes(int T, int K, int n_ffn) {
+  if (T < 1 || K < 1 || n_ffn < 0) return 0;
+  return permute_ws_bytes(T, K, n_ffn);
+}
+
+moe_status moe_permute(const void* x, int dtype, const int32_t* topk_idx, int T, int H, int K,
+                       int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
+                       int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !topk_idx || !offsets || !x_perm || !row_src || !slot_row || !ws) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || H % 8 || K < 1 || n_ffn < 0 || n_ffn > kMaxFfn ||
+      !fits_i32((long long)T * K))
+    return MOE_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_idx, 4) || !aligned(offsets, 4) ||
+      !aligned(row_src, 4) || !aligned(slot_row, 4) || !aligned(ws, 16))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < permute_ws_bytes(T, K, n_ffn)) return MOE_ERR_WORKSPACE;
+  return launched(launch_permute(x, dtype, topk_idx, T, H, K, n_ffn, offsets, x_perm, row_src,
+                                 slot_row, ws, (hipStream_t)stream));
+}
+
+size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype) {
+  if (rows_cap < 1 || n_ffn < 0 || I < 1 || !dtype_ok(dtype)) return 0;
+  return ffn_ws_bytes(rows_cap, n_ffn, I, dtype);
+}
+
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
+                          int H, int I, const void* w13, const void* w2, int dtype, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!x_perm || !offsets || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (rows_cap < 1 || n_ffn < 0 || n_ffn > kMaxFfn || H < 1 || I < 1) return MOE_ERR_SHAPE;
+  if (dtype == MOE_BF16 && (H % 128 || I % 64)) return MOE_ERR_SHAPE;
+  if (dtype == MOE_F32 && (long long)rows_cap / 32 + n_ffn + 8 > 65535) return MOE_ERR_SHAPE;
+  const size_t a = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(x_perm, a) || !aligned(w13, a) || !aligned(w2, a) || !aligned(y_perm, a) ||
+      !aligned(offsets, 4) || !aligned(ws, 256))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < ffn_ws_bytes(rows_cap, n_ffn, I, dtype)) return MOE_ERR_WORKSPACE;
+  if (n_ffn == 0) return MOE_OK;
+  return launched(launch_expert_ffn(x_perm, offsets, rows_cap, n_ffn, H, I, w13, w2, dtype, y_perm,
+                                    ws, (hipStream_t)stream));
+}
+
+moe_status moe_zero_experts(const void* x, int dtype, const int32_t* topk_idx,
+                            const float* topk_gate, int T, int H, int K, int n_ffn, float* y_acc,
+                            void* stream) {
+  if (!x || !topk_idx || !topk_gate || !y_acc) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || H % 8 || K < 1 || n_ffn < 0 || !fits_i32((long long)T * K))
+    return MOE_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y_acc, 16) || !aligned(topk_idx, 4) || !aligned(topk_gate, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_zero_experts(x, dtype, topk_idx, topk_gate, T, H, K, n_ffn, y_acc,
+                                      (hipStream_t)stream));
+}
+
+moe_status moe_combine(const void* y_perm, int dtype, const int32_t* slot_row,
+                       const float* topk_gate, float ffn_scale, const float* y_acc, int T, int H,
+                       int K, void* y, void* stream) {
+  if (!y_perm || !slot_row || !topk_gate || !y_acc || !y) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || H % 8 || K < 1 || K > kMaxKCombine || !fits_i32((long long)T * K))
+    return MOE_ERR_SHAPE;
+  if (!aligned(y_perm, 16) || !aligned(y_acc, 16) || !aligned(y, 16) || !aligned(slot_row, 4) ||
+      !aligned(topk_gate, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_combine(y_perm, dtype, slot_row, topk_gate, ffn_scale, y_acc, T, H, K, y,
+                                 (hipStream_t)stream));
+}
+
+}  // extern "C"

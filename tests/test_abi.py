@@ -1,0 +1,125 @@
+"""The C-ABI boundary on the host: the library loads, exports every function
+include/moe_mi355x.h declares, and rejects bad arguments with status codes
+before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_02_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+OK, NULL, SHAPE, DTYPE, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # never dereferenced: validation fails first or only sizes are read
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe._SIGS)
+
+
+def test_status_strings():
+    lib = moe.lib()
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(WS) == b"workspace too small"
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries():
+    lib = moe.lib()
+    assert lib.moe_permute_workspace_bytes(8192, 12, 512) >= 512 * 128 * 4
+    assert lib.moe_permute_workspace_bytes(0, 12, 512) == 0
+    # the FFN workspace holds the intermediate activations: rows x I elements
+    b16 = lib.moe_expert_ffn_workspace_bytes(98304, 512, 2048, 1)
+    f32 = lib.moe_expert_ffn_workspace_bytes(98304, 512, 2048, 0)
+    assert b16 >= 98304 * 2048 * 2 and f32 >= 98304 * 2048 * 4
+    assert lib.moe_expert_ffn_workspace_bytes(10, 4, 64, 7) == 0
+
+
+def test_router_logits_validation():
+    f = moe.lib().moe_router_logits
+    assert f(None, 1, FAKE, 4, 64, 8, FAKE, None) == NULL
+    assert f(FAKE, 5, FAKE, 4, 64, 8, FAKE, None) == DTYPE
+    assert f(FAKE, 1, FAKE, 0, 64, 8, FAKE, None) == SHAPE
+    assert f(FAKE, 1, FAKE, 4, 64, 0, FAKE, None) == SHAPE
+    assert f(P(0x10001), 1, FAKE, 4, 64, 8, FAKE, None) == ALIGN
+
+
+def test_route_validation():
+    f = moe.lib().moe_route
+    args = [FAKE, FAKE, 16, 24, 4, FAKE, FAKE, FAKE, None, None]
+    a = list(args); a[0] = None
+    assert f(*a) == NULL
+    a = list(args); a[4] = 0
+    assert f(*a) == SHAPE
+    a = list(args); a[4] = 25                     # K > E
+    assert f(*a) == SHAPE
+    a = list(args); a[3] = 1025; a[4] = 4         # E beyond one wave's 16 keys per lane
+    assert f(*a) == SHAPE
+    a = list(args); a[2] = 1 << 28; a[4] = 16     # T*K >= 2^31
+    assert f(*a) == SHAPE
+    a = list(args); a[8] = P(0x10002)
+    assert f(*a) == ALIGN
+
+
+def test_permute_validation():
+    f = moe.lib().moe_permute
+    need = moe.lib().moe_permute_workspace_bytes(64, 4, 16)
+    args = [FAKE, 1, FAKE, 64, 256, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, need, None]
+    a = list(args); a[11] = None
+    assert f(*a) == NULL
+    a = list(args); a[4] = 250                    # H not a multiple of 8
+    assert f(*a) == SHAPE
+    a = list(args); a[6] = 5000                   # too many FFN experts
+    assert f(*a) == SHAPE
+    a = list(args); a[12] = need - 1
+    assert f(*a) == WS
+    a = list(args); a[8] = P(0x10008)             # x_perm not 16-byte aligned
+    assert f(*a) == ALIGN
+
+
+def test_expert_ffn_validation():
+    f = moe.lib().moe_expert_ffn
+    need = moe.lib().moe_expert_ffn_workspace_bytes(256, 16, 1024, 1)
+    args = [FAKE, FAKE, 256, 16, 2048, 1024, FAKE, FAKE, 1, FAKE, FAKE, need, None]
+    a = list(args); a[6] = None
+    assert f(*a) == NULL
+    a = list(args); a[4] = 2000                   # bf16 path needs H % 128 == 0
+    assert f(*a) == SHAPE
+    a = list(args); a[5] = 1000                   # and I % 64 == 0
+    assert f(*a) == SHAPE
+    a = list(args); a[11] = need - 1
+    assert f(*a) == WS
+    a = list(args); a[8] = 9
+    assert f(*a) == DTYPE
+    a = list(args); a[3] = 0                      # no FFN experts: nothing to do
+    assert f(*a) == OK
+
+
+def test_zero_and_combine_validation():
+    z = moe.lib().moe_zero_experts
+    assert z(FAKE, 1, FAKE, FAKE, 8, 100, 4, 2, FAKE, None) == SHAPE
+    assert z(FAKE, 1, FAKE, None, 8, 128, 4, 2, FAKE, None) == NULL
+    c = moe.lib().moe_combine
+    assert c(FAKE, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE, 8, 128, 2000, FAKE, None) == SHAPE
+    assert c(FAKE, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE, 8, 128, 4, P(0x10004), None) == ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_router_logits(x, torch.zeros((8, 64)), torch.zeros((4, 8)))

@@ -1,0 +1,153 @@
+"""Parity at the full LongCat-Flash MoE shapes (hidden 6144, 512 FFN + 256
+identity experts, intermediate 2048, K = 12; 38.65 GB of bf16 expert weights
+resident), in the launch configuration the benchmark times.
+
+Integer stages are checked in full on the GPU's own inputs (routing on the
+GPU's logits, dispatch on the GPU's ids).  Floating-point stages are checked
+on samples the oracle computes one by one: logits of sampled tokens, FFN rows
+of sampled experts (first, last and random rows, so several m-tiles of a heavy
+expert), identity-expert rows, combine rows, and whole-layer outputs of
+sampled tokens computed from the inputs alone (with the flip rule)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_02_amd as moe
+import workload
+from _parity import FLIP_MARGIN, LOGIT_TOL, THREADS, TOL, device, forward, host, margins, normwise
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+FULL = ["prefill_bf16", "decode_bf16", "skewed_bf16"]
+
+
+@pytest.fixture(scope="module")
+def shared_weights():
+    cfg = workload.CONFIGS["prefill_bf16"]
+    dev = device()
+    print("\n[setup] drawing 38.65 GB of expert weights on the GPU", flush=True)
+    w13, w2 = workload.make_expert_weights(cfg, dev)
+    wr = workload.make_router(cfg).to(dev)
+    torch.cuda.synchronize()
+    yield w13, w2, wr
+    del w13, w2, wr
+    torch.cuda.empty_cache()
+
+
+def _expert_host(w13, w2, e):
+    return host(w13[e]), host(w2[e])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_scale_layer(name, shared_weights):
+    cfg = workload.CONFIGS[name]
+    w13, w2, wr = shared_weights
+    dev = device()
+    rng = np.random.default_rng(1234)
+    print(f"\n[case] {name}: T={cfg.T}", flush=True)
+    inp = dict(x=workload.make_x(cfg).to(dev), w_router=wr,
+               bias=workload.make_bias(cfg).to(dev), w13=w13, w2=w2)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    forward(cfg, inp, buf)
+    K, N, tol = cfg.K, cfg.N, TOL[cfg.dtype]
+    x_t = inp["x"]
+    bias = host(inp["bias"])
+    wr_h = host(wr)
+
+    # S0: logits of sampled tokens
+    toks = np.unique(np.r_[0, cfg.T - 1, rng.choice(cfg.T, min(cfg.T, 30), False)])
+    xs = host(x_t[torch.from_numpy(toks).to(dev)])
+    l_gpu = host(buf["logits"])
+    e0 = normwise(l_gpu[toks], oracle.router_logits(xs, wr_h, threads=THREADS))
+    assert e0 <= LOGIT_TOL, e0
+
+    # S1: routing of every token on the GPU's logits, bit-exact
+    idx_ref, gate_ref, counts_ref = oracle.route(l_gpu, bias, K)
+    idx = host(buf["topk_idx"])
+    np.testing.assert_array_equal(idx, idx_ref)
+    counts = host(buf["counts"])
+    np.testing.assert_array_equal(counts, counts_ref)
+    assert counts.sum() == cfg.T * K
+    e1 = normwise(host(buf["topk_gate"]), gate_ref)
+    assert e1 <= LOGIT_TOL, e1
+    assert int(host(buf["status"])[0]) == 0
+
+    # S2: dispatch of every selection, bit-exact (row gather checked on the GPU)
+    off_ref, rs_ref, slot_ref = oracle.permute(idx, N)
+    S = int(off_ref[-1])
+    np.testing.assert_array_equal(host(buf["offsets"]), off_ref)
+    np.testing.assert_array_equal(host(buf["row_src"][:S]), rs_ref)
+    np.testing.assert_array_equal(host(buf["slot_row"]), slot_ref)
+    rs = torch.from_numpy(rs_ref.astype(np.int64)).to(dev)
+    assert torch.equal(buf["x_perm"][:S], x_t[rs // K])
+
+    # S3: FFN rows of sampled experts on the GPU's grouped rows
+    ffn_counts = counts[:N]
+    live = np.nonzero(ffn_counts)[0]
+    order = live[np.argsort(ffn_counts[live])]
+    experts = np.unique([order[0], order[len(order) // 2], order[-1], live[0], live[-1]])
+    e3 = 0.0
+    for e in experts:
+        a, b = int(off_ref[e]), int(off_ref[e + 1])
+        m = b - a
+        rows = np.arange(m) if m <= 40 else np.unique(np.r_[0:12, m - 12:m,
+                                                            rng.choice(m, 16, False)])
+        w13e, w2e = _expert_host(w13, w2, int(e))
+        sel = torch.from_numpy((a + rows).astype(np.int64)).to(dev)
+        ref = oracle.ffn_rows(host(buf["x_perm"][sel]), w13e, w2e, threads=THREADS)
+        err = normwise(host(buf["y_perm"][sel]), ref)
+        print(f"  expert {int(e)} ({m} rows): y_perm normwise {err:.3e}", flush=True)
+        e3 = max(e3, err)
+    assert e3 <= tol, e3
+
+    # S4: identity-expert rows of sampled tokens on the GPU's ids and gates
+    gate = host(buf["topk_gate"]).astype(np.float64)
+    tsel = torch.from_numpy(toks).to(dev)
+    yacc_ref = oracle.zero_experts(xs, idx[toks], gate[toks], N)
+    e4 = normwise(host(buf["y_acc"][tsel]), yacc_ref)
+    assert e4 <= 1e-6, e4
+
+    # S5: combine of sampled tokens on the GPU's y_perm rows
+    slots = slot_ref.reshape(cfg.T, K)[toks]
+    used = slots[slots >= 0]
+    remap = np.full(slots.shape, -1, np.int32)
+    remap[slots >= 0] = np.arange(used.size)
+    yp = host(buf["y_perm"][torch.from_numpy(used.astype(np.int64)).to(dev)]).astype(np.float64)
+    y_ref = oracle.combine(yp, remap.ravel(), idx[toks], gate[toks], cfg.scale,
+                           host(buf["y_acc"][tsel]).astype(np.float64), N)
+    e5 = normwise(host(buf["y"][tsel]), y_ref)
+    assert e5 <= tol, e5
+
+    # end to end: a few tokens from the inputs alone, expert by expert
+    ends = np.unique(np.r_[0, cfg.T - 1, rng.choice(cfg.T, 4, False)])
+    xe = host(x_t[torch.from_numpy(ends).to(dev)])
+    l32 = oracle.router_logits(xe, wr_h, threads=THREADS).astype(np.float32)
+    i_o, _, _ = oracle.route(l32, bias, K)
+    i_g = idx[ends]
+    flips = 0
+    y_e = np.empty((ends.size, cfg.H))
+    for n in range(ends.size):
+        choice = i_o[n]
+        if set(i_g[n]) != set(i_o[n]):
+            m = margins(l32[n:n + 1], bias, K)[0]
+            assert m < FLIP_MARGIN, m
+            choice = i_g[n]
+            flips += 1
+        g = oracle.gates(l32[n:n + 1], choice[None, :])
+        ffn_slots = [k for k in range(K) if choice[k] < N]
+        outs = np.zeros((max(1, len(ffn_slots)), cfg.H))
+        slot_map = np.full(K, -1, np.int32)
+        for r, k in enumerate(ffn_slots):
+            w13e, w2e = _expert_host(w13, w2, int(choice[k]))
+            outs[r] = oracle.ffn_row(xe[n], w13e, w2e)
+            slot_map[k] = r
+        yacc = oracle.zero_experts(xe[n:n + 1], choice[None, :], g, N)
+        y_e[n] = oracle.combine(outs, slot_map, choice[None, :], g, cfg.scale, yacc, N)[0]
+    e_end = normwise(host(buf["y"][torch.from_numpy(ends).to(dev)]), y_e)
+    print(f"  {name}: logits {e0:.2e} gates {e1:.2e} y_perm {e3:.2e} y_acc {e4:.2e} "
+          f"y {e5:.2e} end-to-end {e_end:.2e} (flips {flips}); S={S}, "
+          f"active experts {live.size}", flush=True)
+    assert e_end <= tol, e_end
+    del buf, inp
+    torch.cuda.empty_cache()

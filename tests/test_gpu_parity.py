@@ -1,0 +1,178 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle, at
+sizes the oracle finishes in seconds: several tiles, ragged tails, and the
+degenerate routings of the method."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_02_amd as moe
+import workload
+from _parity import (TOL, check_end_to_end, device, forward, host, inputs_on_host, normwise,
+                     stage_checks)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, bias=None):
+    dev = device()
+    print(f"\n[case] {cfg}", flush=True)
+    inp = workload.make_inputs(cfg, dev)
+    if bias is not None:
+        inp["bias"] = torch.as_tensor(bias, dtype=torch.float32, device=dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    forward(cfg, inp, buf)
+    return inp, buf
+
+
+def _e2e(cfg, inp, buf, tokens=None):
+    h = inputs_on_host(inp)
+    err, flips = check_end_to_end(cfg, h["x"], h["w_router"], h["bias"], h["w13"], h["w2"],
+                                  host(buf["y"]), host(buf["topk_idx"]), tokens)
+    print(f"end-to-end normwise {err:.3e}, flipped tokens {flips}", flush=True)
+    assert err <= TOL[cfg.dtype]
+    return err
+
+
+def test_tiny_fp32_layer():
+    cfg = workload.CONFIGS["tiny_fp32"]
+    inp, buf = _run(cfg)
+    print(stage_checks(cfg, inp, buf))
+    _e2e(cfg, inp, buf)
+
+
+def test_mid_bf16_layer():
+    cfg = workload.CONFIGS["mid_bf16"]
+    inp, buf = _run(cfg)
+    counts = host(buf["counts"])[:cfg.N]
+    order = np.argsort(counts)
+    experts = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    print(stage_checks(cfg, inp, buf, ffn_experts=experts))
+    tokens = np.r_[0:24, cfg.T - 24:cfg.T, np.random.default_rng(0).choice(cfg.T, 48, False)]
+    _e2e(cfg, inp, buf, np.unique(tokens))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 63, 65, 333])
+def test_ragged_token_counts(T, dtype):
+    cfg = workload.MoEConfig("ragged", T=T, H=256, N=8, Z=4, I=128, K=3, dtype=dtype,
+                             sigma_w=0.05, bias_lo=-0.1, bias_hi=0.1, scale=1.5)
+    inp, buf = _run(cfg)
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
+
+
+def test_multi_tile_experts_bf16():
+    # ~660 rows per FFN expert: several 256-row m-tiles and a ragged last one
+    cfg = workload.MoEConfig("multitile", T=2000, H=384, N=4, Z=2, I=192, K=2, dtype="bf16",
+                             sigma_w=0.05, bias_lo=-0.01, bias_hi=0.01, scale=1.0)
+    inp, buf = _run(cfg)
+    assert host(buf["counts"])[:cfg.N].max() > 512
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
+
+
+def test_k_equals_e_picks_every_expert():
+    cfg = workload.MoEConfig("k_eq_e", T=70, H=128, N=5, Z=3, I=64, K=8, dtype="bf16",
+                             sigma_w=0.05, bias_lo=-0.1, bias_hi=0.1, scale=1.0)
+    inp, buf = _run(cfg)
+    stage_checks(cfg, inp, buf)
+    assert (host(buf["counts"]) == cfg.T).all()
+    np.testing.assert_allclose(host(buf["topk_gate"]).sum(1), 1.0, atol=1e-5)
+    _e2e(cfg, inp, buf)
+
+
+def test_all_zero_expert_routing_returns_scaled_x():
+    cfg = workload.MoEConfig("all_zero", T=130, H=256, N=6, Z=4, I=128, K=3, dtype="bf16",
+                             sigma_w=0.05, bias_lo=0.0, bias_hi=0.0, scale=1.0)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[cfg.N:] = 1e3
+    inp, buf = _run(cfg, bias)
+    assert (host(buf["topk_idx"]) >= cfg.N).all()
+    assert int(host(buf["offsets"])[-1]) == 0
+    assert (host(buf["slot_row"]) == -1).all()
+    x = host(inp["x"]).astype(np.float64)
+    g = host(buf["topk_gate"]).astype(np.float64).sum(1, keepdims=True)
+    assert normwise(host(buf["y"]), x * g) <= TOL["bf16"]
+    _e2e(cfg, inp, buf)
+
+
+def test_all_ffn_routing_has_no_identity_term():
+    cfg = workload.MoEConfig("all_ffn", T=130, H=256, N=6, Z=4, I=128, K=3, dtype="bf16",
+                             sigma_w=0.05, bias_lo=0.0, bias_hi=0.0, scale=2.0)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[cfg.N:] = -1e3
+    inp, buf = _run(cfg, bias)
+    assert (host(buf["topk_idx"]) < cfg.N).all()
+    assert (host(buf["y_acc"]) == 0).all()
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
+
+
+def test_route_ties_signed_zero_and_masking_are_bit_exact():
+    dev = device()
+    rng = np.random.default_rng(11)
+    T, E, K = 200, 96, 8
+    # quantised logits: many exact ties; signed zeros; some masked experts
+    l = (rng.integers(-4, 5, (T, E)) * 0.125).astype(np.float32)
+    l[l == 0] = np.where(rng.random((l == 0).sum()) < 0.5, -0.0, 0.0)
+    b = np.zeros(E, np.float32)
+    b[rng.choice(E, 10, False)] = -np.inf
+    lt = torch.from_numpy(l).to(dev)
+    bt = torch.from_numpy(b).to(dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+    moe.moe_route(lt, bt, K, idx, gate, counts, status)
+    torch.cuda.synchronize()
+    i_ref, g_ref, c_ref = oracle.route(l, b, K)
+    np.testing.assert_array_equal(host(idx), i_ref)
+    np.testing.assert_array_equal(host(counts), c_ref)
+    assert normwise(host(gate), g_ref) <= 1e-6
+    assert int(host(status)[0]) == 0
+    # K beyond the unmasked experts: masked ones follow, lowest id first
+    moe.moe_route(lt, bt, 90, torch.empty((T, 90), dtype=torch.int32, device=dev),
+                  torch.empty((T, 90), dtype=torch.float32, device=dev), counts, status)
+    torch.cuda.synchronize()
+    assert int(host(status)[0]) == 0
+
+
+def test_route_flags_nan_keys():
+    dev = device()
+    l = torch.zeros((4, 24), dtype=torch.float32, device=dev)
+    l[2, 5] = float("nan")
+    b = torch.zeros(24, dtype=torch.float32, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+    moe.moe_route(l, b, 4, torch.empty((4, 4), dtype=torch.int32, device=dev),
+                  torch.empty((4, 4), dtype=torch.float32, device=dev),
+                  torch.empty(24, dtype=torch.int32, device=dev), status)
+    torch.cuda.synchronize()
+    assert int(host(status)[0]) == 1
+
+
+def test_forward_is_bitwise_deterministic():
+    cfg = workload.CONFIGS["mid_bf16"].replace(T=1024)
+    inp, buf = _run(cfg)
+    y1 = buf["y"].clone()
+    yp1 = buf["y_perm"].clone()
+    forward(cfg, inp, buf)
+    assert torch.equal(buf["y"], y1)
+    S = int(host(buf["offsets"])[-1])
+    assert torch.equal(buf["y_perm"][:S], yp1[:S])
+
+
+def test_rows_past_the_grouped_rows_are_untouched():
+    cfg = workload.CONFIGS["tiny_fp32"].replace(T=100)
+    dev = device()
+    inp = workload.make_inputs(cfg, dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    buf["x_perm"].fill_(123.0)
+    buf["y_perm"].fill_(-7.0)
+    buf["row_src"].fill_(-5)
+    forward(cfg, inp, buf)
+    S = int(host(buf["offsets"])[-1])
+    assert S < cfg.T * cfg.K
+    assert (host(buf["x_perm"][S:]) == 123.0).all()
+    assert (host(buf["y_perm"][S:]) == -7.0).all()
+    assert (host(buf["row_src"][S:]) == -5).all()
