@@ -1,0 +1,190 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+One step = the six calls of one forward pass (router scores, routing,
+dispatch, expert FFNs, identity experts, combine) over one batch of synthetic
+input already resident in HBM, enqueued back to back on one stream.  Default
+workload: the full-scale prefill-shaped layer (T = 8192 tokens, hidden 6144,
+512 SwiGLU FFN experts of intermediate 2048 + 256 identity experts, K = 12,
+38.65 GB of bf16 expert weights on the GPU).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (the
+gate/up expert GEMM, HBM-bound at these shapes) from per-kernel HIP events
+recorded in the timed region, and the oracle's CPU throughput on a bounded
+sample of the same workload.
+
+    python bench.py [--steps 20] [--warmup 3] [--workload prefill_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_moe_layer_02_amd as moe  # noqa: E402
+import workload  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM MFMA util and HBM GB/s vs peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="prefill_bf16", choices=sorted(workload.CONFIGS))
+    p.add_argument("--cpu-tokens", type=int, default=96,
+                   help="tokens of the oracle's CPU sample (0 = skip)")
+    p.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    return p.parse_args()
+
+
+def algorithmic(cfg, counts, S):
+    """Bytes the method must move / FLOPs it must do, per kernel of interest.
+    Expert weights count once per active expert; activations once per row."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    active = int((counts[:cfg.N] > 0).sum())
+    H, I = cfg.H, cfg.I
+    w13 = active * 2 * I * H * es
+    w2 = active * H * I * es
+    gateup_bytes = w13 + S * H * es + S * I * es        # weights + x_perm rows + hh rows
+    down_bytes = w2 + S * I * es + S * H * es           # weights + hh rows + y_perm rows
+    gateup_flops = 2.0 * S * H * 2 * I
+    down_flops = 2.0 * S * I * H
+    return dict(active=active, gateup_bytes=gateup_bytes, down_bytes=down_bytes,
+                gateup_flops=gateup_flops, down_flops=down_flops)
+
+
+def cpu_baseline(cfg, inp, n_tokens):
+    """The oracle, single-threaded, on n_tokens sampled tokens through all six
+    stages.  Copies of expert weights to the host are not timed."""
+    import oracle
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(cfg.T, n_tokens, replace=False))
+    dev = inp["x"].device
+    x = inp["x"][torch.from_numpy(toks).to(dev)].float().cpu().numpy()
+    wr = inp["w_router"].cpu().numpy()
+    b = inp["bias"].cpu().numpy()
+    K, N = cfg.K, cfg.N
+    spent = 0.0
+    t0 = time.perf_counter()
+    l32 = oracle.router_logits(x, wr).astype(np.float32)
+    idx, gate, _ = oracle.route(l32, b, K)
+    off, rs, slot = oracle.permute(idx, N)
+    spent += time.perf_counter() - t0
+    xp = x[rs // K]
+    yp = np.empty((rs.size, cfg.H))
+    for e in np.nonzero(np.diff(off))[0]:
+        a, c = int(off[e]), int(off[e + 1])
+        w13e = inp["w13"][e].float().cpu().numpy()
+        w2e = inp["w2"][e].float().cpu().numpy()
+        t0 = time.perf_counter()
+        yp[a:c] = oracle.ffn_rows(xp[a:c], w13e, w2e)
+        spent += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    yacc = oracle.zero_experts(x, idx, gate, N)
+    oracle.combine(yp, slot, idx, gate, cfg.scale, yacc, N)
+    spent += time.perf_counter() - t0
+    return dict(value=n_tokens / spent, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n_tokens} of {cfg.T} tokens of {cfg.name}, all six stages, "
+                       f"single-threaded fp64 oracle ({spent:.1f} s of CPU; weight copies "
+                       f"to the host not timed)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    cfg = workload.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name}: drawing inputs on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    inp = workload.make_inputs(cfg, dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        moe.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K,
+                    cfg.scale, buf)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+
+    moe.moe_profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    moe.moe_profile_enable(False)
+    ms = start.elapsed_time(end) / args.steps
+    kern = moe.moe_profile_summary()
+
+    counts = buf["counts"].cpu().numpy()
+    S = int(buf["offsets"][-1].item())
+    alg = algorithmic(cfg, counts, S)
+    kname = "ffn_gateup_bf16" if cfg.dtype == "bf16" else "ffn_gateup_f32"
+    n_launch, tot = kern[kname]
+    k_ms = tot / n_launch
+    achieved = alg["gateup_bytes"] / (k_ms * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel=kname, kernel_ms=round(k_ms, 4),
+                    algorithmic_bytes=alg["gateup_bytes"],
+                    mfma_frac=round(alg["gateup_flops"] / (k_ms * 1e-3) / 1e12
+                                    / MFMA_BF16_PEAK_TFLOPS, 4))
+    d_n, d_tot = kern.get("ffn_down_bf16", kern.get("ffn_down_f32", (1, float("nan"))))
+    d_ms = d_tot / d_n
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,sigma) weights; no checkpoint)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "ffn_experts": cfg.N,
+                   "zero_experts": cfg.Z, "intermediate": cfg.I, "top_k": cfg.K,
+                   "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"]},
+        "roofline": roofline,
+        "down_gemm": {"kernel_ms": round(d_ms, 4),
+                      "hbm_frac": round(alg["down_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(alg["down_flops"] / (d_ms * 1e-3) / 1e12
+                                         / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels_us": {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()},
+    }
+    if args.cpu_tokens > 0:
+        print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_tokens, cfg.T))
+    else:
+        result["cpu_baseline"] = None
+    if args.kernels:
+        for k, (n, t) in kern.items():
+            print(f"{k:28s} {n:5d} launches  {t / n * 1e3:10.1f} us", file=sys.stderr)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

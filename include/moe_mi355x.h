@@ -137,6 +137,18 @@ moe_status moe_combine(const void *y_perm, int dtype, const int32_t *slot_row,
                        const float *topk_gate, float ffn_scale, const float *y_acc,
                        int T, int H, int K, void *y, void *stream);
 
+/* Diagnostics (not part of the layer): opt-in per-kernel timing.  While
+ * enabled, each kernel the calls above enqueue is bracketed by two HIP events
+ * recorded on its stream.  moe_profile_enable(1) starts a new session (the
+ * previous records are dropped), (0) stops recording; it returns the previous
+ * state.  moe_profile_summary waits for the recorded events and writes one
+ * line "kernel_name launches total_ms" per kernel into buf (at most len
+ * bytes, NUL-terminated); it returns the length of the full text, or -1 if an
+ * event could not be read.  The session is process-wide; concurrent callers
+ * share it. */
+int moe_profile_enable(int on);
+int moe_profile_summary(char *buf, size_t len);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 

@@ -36,6 +36,8 @@ _SIGS = {
     "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
+    "moe_profile_enable": ([_I], _I),
+    "moe_profile_summary": ([ctypes.c_char_p, ctypes.c_size_t], _I),
 }
 
 
@@ -178,6 +180,27 @@ def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
     _check("moe_combine", lib().moe_combine(
         _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
+
+
+# ------------------------------------------------------------ diagnostics --
+
+def moe_profile_enable(on: bool) -> bool:
+    """Start (True) or stop (False) per-kernel event timing; returns the old state."""
+    return bool(lib().moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_summary() -> dict:
+    """{kernel name: (launches, total ms)} of the current timing session."""
+    n = lib().moe_profile_summary(None, 0)
+    if n < 0:
+        raise RuntimeError("moe_profile_summary: an event could not be read")
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().moe_profile_summary(buf, n + 1)
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
 
 
 # ------------------------------------------------------- buffers + forward --

@@ -106,11 +106,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, const float* gate,
                                int T, int H, int K, int n_ffn, float* y_acc, hipStream_t s) {
   if (dtype == MOE_BF16)
-    zero_experts_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)x, idx, gate, H, K, n_ffn,
-                                                     y_acc);
+    MOE_LAUNCH("zero_experts", s,
+               zero_experts_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)x, idx, gate, H, K,
+                                                                n_ffn, y_acc));
   else
-    zero_experts_kernel<float><<<T, kThreads, 0, s>>>((const float*)x, idx, gate, H, K, n_ffn,
-                                                      y_acc);
+    MOE_LAUNCH("zero_experts", s,
+               zero_experts_kernel<float><<<T, kThreads, 0, s>>>((const float*)x, idx, gate, H,
+                                                                 K, n_ffn, y_acc));
   return hipGetLastError();
 }
 
@@ -118,11 +120,14 @@ hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row
                           const float* gate, float scale, const float* y_acc, int T, int H,
                           int K, void* y, hipStream_t s) {
   if (dtype == MOE_BF16)
-    combine_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)y_perm, slot_row, gate, scale,
-                                                y_acc, H, K, (bf16*)y);
+    MOE_LAUNCH("combine", s,
+               combine_kernel<bf16><<<T, kThreads, 0, s>>>((const bf16*)y_perm, slot_row, gate,
+                                                           scale, y_acc, H, K, (bf16*)y));
   else
-    combine_kernel<float><<<T, kThreads, 0, s>>>((const float*)y_perm, slot_row, gate, scale,
-                                                 y_acc, H, K, (float*)y);
+    MOE_LAUNCH("combine", s,
+               combine_kernel<float><<<T, kThreads, 0, s>>>((const float*)y_perm, slot_row,
+                                                            gate, scale, y_acc, H, K,
+                                                            (float*)y));
   return hipGetLastError();
 }
 

@@ -310,20 +310,28 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int row
   int* ntiles = (int*)ws;
   int4* tiles = (int4*)((char*)ws + 256);
   void* hh = (char*)ws + 256 + align256(mtmax * sizeof(int4));
-  ffn_tiles<<<1, 1024, 0, s>>>(offsets, n_ffn, bm, rows_cap, (int)mtmax, tiles, ntiles);
+  MOE_LAUNCH("ffn_tiles", s,
+             ffn_tiles<<<1, 1024, 0, s>>>(offsets, n_ffn, bm, rows_cap, (int)mtmax, tiles,
+                                          ntiles));
   if (dtype == MOE_BF16) {
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
-    ffn_mfma_bf16<kBmBf16, kStagesBf16, true><<<groups * 8 * nt1, kThreads, 0, s>>>(
-        (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1, (bf16*)hh);
-    ffn_mfma_bf16<kBmBf16, kStagesBf16, false><<<groups * 8 * nt2, kThreads, 0, s>>>(
-        (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2, (bf16*)y_perm);
+    MOE_LAUNCH("ffn_gateup_bf16", s,
+               ffn_mfma_bf16<kBmBf16, kStagesBf16, true><<<groups * 8 * nt1, kThreads, 0, s>>>(
+                   (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1,
+                   (bf16*)hh));
+    MOE_LAUNCH("ffn_down_bf16", s,
+               ffn_mfma_bf16<kBmBf16, kStagesBf16, false><<<groups * 8 * nt2, kThreads, 0, s>>>(
+                   (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
+                   (bf16*)y_perm));
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
-    ffn_f32<true><<<g1, kThreads, 0, s>>>((const float*)x_perm, (const float*)w13, tiles, ntiles,
-                                          H, I, H, (float*)hh);
-    ffn_f32<false><<<g2, kThreads, 0, s>>>((const float*)hh, (const float*)w2, tiles, ntiles, I,
-                                           I, H, (float*)y_perm);
+    MOE_LAUNCH("ffn_gateup_f32", s,
+               ffn_f32<true><<<g1, kThreads, 0, s>>>((const float*)x_perm, (const float*)w13,
+                                                     tiles, ntiles, H, I, H, (float*)hh));
+    MOE_LAUNCH("ffn_down_f32", s,
+               ffn_f32<false><<<g2, kThreads, 0, s>>>((const float*)hh, (const float*)w2, tiles,
+                                                      ntiles, I, I, H, (float*)y_perm));
   }
   return hipGetLastError();
 }

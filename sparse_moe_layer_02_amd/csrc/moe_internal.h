@@ -49,6 +49,16 @@ __device__ __forceinline__ void lds_barrier() {
 
 inline unsigned ceil_div(size_t a, size_t b) { return (unsigned)((a + b - 1) / b); }
 
+// ---- opt-in per-kernel event timing (profile.hip) --------------------------
+int prof_begin(const char* name, hipStream_t s);   // -1 when timing is off
+void prof_end(int token, hipStream_t s);
+#define MOE_LAUNCH(name, stream, ...)                 \
+  do {                                                \
+    const int moe_tok_ = ::moe::prof_begin(name, stream); \
+    __VA_ARGS__;                                      \
+    ::moe::prof_end(moe_tok_, stream);                \
+  } while (0)
+
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----------
 hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int H, int E,
                                 float* logits, hipStream_t s);

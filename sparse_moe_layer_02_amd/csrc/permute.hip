@@ -179,19 +179,26 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, i
   int32_t* tot = (int32_t*)((char*)ws + align256((size_t)n_ffn * nblk * 4));
   const size_t lds = (size_t)(n_ffn > 0 ? n_ffn : 1) * sizeof(unsigned long long);
   if (n_ffn > 0) {
-    perm_hist<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt);
-    perm_scan_blocks<<<ceil_div(n_ffn, 4), 256, 0, s>>>(cnt, nblk, n_ffn, tot);
+    MOE_LAUNCH("permute_hist", s,
+               perm_hist<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt));
+    MOE_LAUNCH("permute_scan_blocks", s,
+               perm_scan_blocks<<<ceil_div(n_ffn, 4), 256, 0, s>>>(cnt, nblk, n_ffn, tot));
   }
-  perm_scan_experts<<<1, 1024, 0, s>>>(tot, n_ffn, offsets);
-  perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets, row_src,
-                                        slot_row);
+  MOE_LAUNCH("permute_scan_experts", s,
+             perm_scan_experts<<<1, 1024, 0, s>>>(tot, n_ffn, offsets));
+  MOE_LAUNCH("permute_scatter", s,
+             perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets,
+                                                   row_src, slot_row));
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = (int)((size_t)H * esize / 16);
   if (row_vecs <= 256 * 4)
-    perm_gather<4><<<T, 256, 0, s>>>((const i32x4*)x, row_vecs, K, slot_row, (i32x4*)x_perm);
+    MOE_LAUNCH("permute_gather", s,
+               perm_gather<4><<<T, 256, 0, s>>>((const i32x4*)x, row_vecs, K, slot_row,
+                                                (i32x4*)x_perm));
   else
-    perm_gather_long<<<T, 256, 0, s>>>((const i32x4*)x, row_vecs, K, slot_row,
-                                       (i32x4*)x_perm);
+    MOE_LAUNCH("permute_gather", s,
+               perm_gather_long<<<T, 256, 0, s>>>((const i32x4*)x, row_vecs, K, slot_row,
+                                                  (i32x4*)x_perm));
   return hipGetLastError();
 }
 

@@ -133,12 +133,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K,
                         int32_t* idx, float* gate, int32_t* counts, int32_t* status,
                         hipStream_t s) {
-  zero_i32<<<ceil_div(E, 256), 256, 0, s>>>(counts, E);
+  MOE_LAUNCH("route_clear", s, zero_i32<<<ceil_div(E, 256), 256, 0, s>>>(counts, E));
   const unsigned grid = ceil_div(T, kTokensPerBlock);
   const int epl = (E + kWave - 1) / kWave;
-#define MOE_ROUTE(N)                                                                          \
-  route_kernel<N><<<grid, kRouteThreads, 0, s>>>(logits, bias, T, E, K, idx, gate, counts, \
-                                                 status)
+#define MOE_ROUTE(N)                                                                    \
+  MOE_LAUNCH("route_topk", s,                                                          \
+             route_kernel<N><<<grid, kRouteThreads, 0, s>>>(logits, bias, T, E, K, idx, \
+                                                            gate, counts, status))
   if (epl <= 1) MOE_ROUTE(1);
   else if (epl <= 2) MOE_ROUTE(2);
   else if (epl <= 4) MOE_ROUTE(4);

@@ -56,9 +56,11 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
                                 float* logits, hipStream_t s) {
   dim3 grid(ceil_div(E, kTN), ceil_div(T, kTM));
   if (dtype == MOE_BF16)
-    router_fma<bf16><<<grid, kThreads, 0, s>>>((const bf16*)x, w, T, H, E, logits);
+    MOE_LAUNCH("router_logits", s,
+               router_fma<bf16><<<grid, kThreads, 0, s>>>((const bf16*)x, w, T, H, E, logits));
   else
-    router_fma<float><<<grid, kThreads, 0, s>>>((const float*)x, w, T, H, E, logits);
+    MOE_LAUNCH("router_logits", s,
+               router_fma<float><<<grid, kThreads, 0, s>>>((const float*)x, w, T, H, E, logits));
   return hipGetLastError();
 }
 
