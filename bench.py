@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=96,
                    help="tokens of the oracle's CPU sample (0 = skip)")
     p.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="first run one plain device-to-device copy of this many MiB (the "
+                        "reference dispatch that scales HBM byte counters)")
     return p.parse_args()
 
 
@@ -113,6 +116,14 @@ def main():
     inp = workload.make_inputs(cfg, dev)
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     def step():
         moe.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K,

@@ -17,7 +17,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+# MOE_MI355X_LIB selects another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}

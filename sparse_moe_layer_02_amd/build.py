@@ -29,14 +29,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = OUT, defines=()) -> str:
+    """Compile every csrc/*.hip and link them into ``out``.  ``defines`` are
+    extra -D options (tuning variants; the default build uses none)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     cc = hipcc()
     tmp = tempfile.mkdtemp(prefix="moe_build_")
     try:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+            cmd = [cc, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -46,16 +48,21 @@ def build(verbose: bool = False) -> str:
 
         with ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1, 16))) as ex:
             objs = list(ex.map(compile_one, srcs))
-        tmp_out = OUT + f".tmp{os.getpid()}"
+        tmp_out = out + f".tmp{os.getpid()}"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(tmp_out, OUT)
+        os.replace(tmp_out, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return OUT
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    out = OUT
+    if "-o" in args:
+        out = os.path.abspath(args[args.index("-o") + 1])
+    defs = [a[2:] for a in args if a.startswith("-D")]
+    print(build(verbose="-v" in args, out=out, defines=defs))

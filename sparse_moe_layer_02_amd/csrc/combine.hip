@@ -11,6 +11,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxK = 1024;
+constexpr int kBatch = 8;
 
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
@@ -90,12 +91,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
     float acc[8];
     Vec8<float>::load(ar + c, acc);
-    for (int j = 0; j < n; ++j) {
-      float v[8];
-      Vec8<T>::load(y_perm + (size_t)rows[j] * H + c, v);
-      const float w = wts[j];
+    // up to kBatch rows in flight per thread; accumulation stays in slot order
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      float v[kBatch][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+      for (int u = 0; u < kBatch; ++u)
+        if (j0 + u < n) Vec8<T>::load(y_perm + (size_t)rows[j0 + u] * H + c, v[u]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u >= n) break;
+        const float w = wts[j0 + u];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
+      }
     }
     Vec8<T>::store(yr + c, acc);
   }

@@ -12,14 +12,15 @@
 //     of the weight matrix, so every weight tile is fetched from HBM once when
 //     an expert's rows fit one m-tile -- the regime of the full-scale layer,
 //     where the weights (not the MFMA rate) bound the time;
-//   - K is swept in 64-element stages (128 B per row) held in LDS; stages are
-//     filled by global_load_lds_dwordx4 (16 B per lane straight into LDS, no
-//     VGPR staging) and several stages are in flight;
-//   - LDS rows are 128 B with the 16-byte chunks XOR-swizzled by
-//     (row ^ row>>3) & 7, which keeps the ds_read_b128 fragment reads free of
-//     bank conflicts for both 8- and 16-lane phases;
 //   - wave w owns 32 weight rows (two 16-column MFMA blocks) and every row
-//     block of the m-tile; 16-row blocks past the expert's rows are skipped;
+//     block of the m-tile; 32-row groups past the expert's rows are skipped;
+//   - K is swept in kBK-element steps staged in LDS by global_load_lds_dwordx4
+//     (16 B per lane, no VGPR staging; weights non-temporal) in one ring as
+//     deep as the 160 KB of LDS allows for the tile's live rows;
+//   - LDS rows hold one step of one row, their 16-byte chunks XOR-swizzled so
+//     that the fragment reads (16 rows x one chunk per 16 lanes) are free of
+//     bank conflicts: timed on gfx950 they run as fast as linear
+//     ds_read_b128 (an unswizzled 128 B-row layout is 2.4x slower);
 //   - gate/up: weight rows are paired so that a lane holds gate column j and
 //     up column j in the same accumulator slot, and silu(g)*u is applied in
 //     registers before hh is stored (bf16);
@@ -31,17 +32,26 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_FFN_BK
+#define MOE_FFN_BK 64
+#endif
 constexpr int kThreads = 256;
-constexpr int kBK = 64;      // k elements per stage: 128 B per LDS row
-constexpr int kBN = 128;     // weight rows per block
-constexpr int kRowBytes = kBK * 2;
+constexpr int kBK = MOE_FFN_BK;                 // k elements per pipeline step
+constexpr int kRowBytes = kBK * 2;              // bytes per LDS row of a step
+constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per LDS row
+constexpr int kRowsPerInstr = 1024 / kRowBytes; // rows one wave-wide 16 B/lane DMA fills
+constexpr int kBN = 128;                        // weight rows per block
 constexpr int kBmBf16 = 256;
-constexpr int kStagesBf16 = 3;
 constexpr int kBmF32 = 32;
+static_assert(kBK == 32 || kBK == 64, "K step of 32 or 64 elements");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
+// Chunk swizzle of an LDS row, chosen so that 16 lanes reading one chunk of
+// 16 consecutive rows (the MFMA fragment read) hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return kChunks == 8 ? chunk ^ (row & 7) : chunk ^ ((row >> 1) & 3);
+}
 
 // ------------------------------------------------------------ work list --
 // Rows are clamped to [0, rows_cap) and the list to max_tiles entries, so a
@@ -88,49 +98,71 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
 //
 // The K loop is instantiated per number G of live 32-row groups of the m-tile
 // (G = ceil(rows / 32)), chosen once per block: each instance is branch-free,
-// loads only the live A rows and issues only the live MFMAs, so the compiler
-// can overlap fragment reads with matrix-core work.
-template <int BM, int STAGES>
-struct Smem {
-  static constexpr int kStageBytes = (BM + kBN) * kRowBytes;
-  static constexpr int kBytes = STAGES * kStageBytes;
+// loads only the live A rows, issues only the live MFMAs, and lays out as many
+// pipeline stages as fit the 160 KB of LDS for its stage size
+// ((32G + 128) rows x 128 B): 8 stages at G = 1 (decode-sized tiles) down to
+// 3 at G = 8.  The weight tiles in flight per CU -- what sustains HBM
+// bandwidth when the weights dominate -- grow as the activation tile shrinks.
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kCachePolicyNT = 2;   // non-temporal: weights are streamed once
+
+// One ring of S steps, each step = the live activation rows plus the 128
+// weight rows over kBK k values, as deep as the 160 KB of LDS allows.
+// Loads complete in issue order, so the wait for step kt also waits for every
+// older load: separate rings for the two operands would not give either one
+// more time in flight.  S is therefore what sets the bytes in flight per CU.
+template <int G>
+struct Pipe {
+  static constexpr int kAq = (32 * G / kRowsPerInstr + 3) / 4;   // A DMA per wave per step
+  static constexpr int kArows = kAq * 4 * kRowsPerInstr;         // >= 32G rows (clamped extras)
+  static constexpr int kBq = kBN / kRowsPerInstr / 4;            // B DMA per wave per step
+  static constexpr int kStageBytes = (kArows + kBN) * kRowBytes;
+  static constexpr int kFit = kLdsBytes / kStageBytes;
+  static constexpr int S = kFit > 16 ? 16 : kFit;
+  static constexpr int kLoads = kAq + kBq;
+  static_assert(S >= 3, "pipeline needs three steps");
+  static_assert(kLoads * (S - 2) < 64, "vmcnt range");
+  static_assert(kArows <= kBmBf16, "A source table size");
 };
 
-template <int G, int BM, int STAGES>
+// Every step issues the same loads -- past the end they read one fixed 16-byte
+// line into a slot that is never read -- so every wait count is a constant.
+template <int G>
 __device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_src,
-                                             const bf16* const* b_src, int KD, int wave, int lane,
-                                             f32x4 (&acc)[BM / 16][2]) {
-  constexpr int kStageBytes = Smem<BM, STAGES>::kStageBytes;
-  constexpr int kAq = G;        // A load instructions per wave: 4 waves x 8 rows x G = 32G rows
-  constexpr int kLoads = kAq + kBN / 32;       // load instructions per wave per stage
+                                             const bf16* const* b_src, const bf16* a_dummy,
+                                             const bf16* b_dummy, int KD, int wave, int lane,
+                                             f32x4 (&acc)[kBmBf16 / 16][2]) {
+  using P = Pipe<G>;
+  constexpr int S = P::S;
   const int KT = KD / kBK;
-  auto issue = [&](int stage, int k0) {
-    char* sb = smem + stage * kStageBytes;
+  auto issue = [&](int kt) {
+    char* sb = smem + (kt % S) * P::kStageBytes;
+    const bool real = kt < KT;
+    const int k0 = real ? kt * kBK : 0;
 #pragma unroll
-    for (int q = 0; q < kAq; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+    for (int q = 0; q < P::kAq; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? a_src[q] + k0 : a_dummy),
                                        (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int q = 0; q < kBN / 32; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
-                                       (lds_void*)(sb + BM * kRowBytes + (wave + 4 * q) * 1024),
-                                       16, 0, 0);
+    for (int q = 0; q < P::kBq; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? b_src[q] + k0 : b_dummy),
+                                       (lds_void*)(sb + P::kArows * kRowBytes +
+                                                   (wave + 4 * q) * 1024),
+                                       16, 0, kCachePolicyNT);
   };
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s * kBK);
+  for (int j = 0; j < S - 1; ++j) issue(j);
 
   const int rB0 = 32 * wave + (lane & 15);
   const int rB1 = rB0 + 16;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + STAGES - 1 <= KT) wait_vmcnt<kLoads * (STAGES - 2)>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * kBK);
-    const char* As = smem + (kt % STAGES) * kStageBytes;
-    const char* Bs = As + BM * kRowBytes;
+    wait_vmcnt<P::kLoads * (S - 2)>();   // step kt has landed (this wave's loads)
+    lds_barrier();                       // ... and every wave's; slot kt-1 is free
+    issue(kt + S - 1);
+    const char* As = smem + (kt % S) * P::kStageBytes;
+    const char* Bs = As + P::kArows * kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kBK / 32; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
       const bf16x8 b0 = *(const bf16x8*)(Bs + rB0 * kRowBytes + swz(rB0, ch) * 16);
       const bf16x8 b1 = *(const bf16x8*)(Bs + rB1 * kRowBytes + swz(rB1, ch) * 16);
@@ -147,13 +179,15 @@ __device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_sr
       }
     }
   }
+  wait_vmcnt<0>();   // the past-the-end loads land before the block exits
 }
 
-template <int BM, int STAGES, bool GATEUP>
+template <bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const int4* __restrict__ tiles,
     const int* __restrict__ ntiles, int KD, int I, int H, int NT, bf16* __restrict__ C) {
-  __shared__ __attribute__((aligned(1024))) char smem[Smem<BM, STAGES>::kBytes];
+  constexpr int BM = kBmBf16;
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
@@ -165,25 +199,26 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int lr = lane >> 3;      // row within an 8-row load group
-  const int lc = lane & 7;       // 16-byte slot within the LDS row
+  const int lr = lane / kChunks;   // row within the rows one DMA instruction fills
+  const int lc = lane % kChunks;   // 16-byte slot within the LDS row
 
-  // global source of this lane's 16-byte loads (k offset added per stage);
+  // global source of this lane's 16-byte loads (k offset added per step);
   // rows past the tile are clamped to its last row (never used)
-  const bf16* a_src[BM / 32];
+  constexpr int kAsrc = BM / kRowsPerInstr / 4;
+  const bf16* a_src[kAsrc];
 #pragma unroll
-  for (int q = 0; q < BM / 32; ++q) {
-    const int r = (wave + 4 * q) * 8 + lr;
+  for (int q = 0; q < kAsrc; ++q) {
+    const int r = (wave + 4 * q) * kRowsPerInstr + lr;
     a_src[q] = A + (size_t)(row0 + min(r, rows - 1)) * KD + swz(r, lc) * 8;
   }
   const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
   const bf16* wexp = W + (size_t)e * wrows * KD;
-  const bf16* b_src[kBN / 32];
+  const bf16* b_src[kBN / kRowsPerInstr / 4];
 #pragma unroll
-  for (int q = 0; q < kBN / 32; ++q) {
-    const int r = (wave + 4 * q) * 8 + lr;
+  for (int q = 0; q < kBN / kRowsPerInstr / 4; ++q) {
+    const int r = (wave + 4 * q) * kRowsPerInstr + lr;
     int wr;
-    if (GATEUP) {
+    if (GATEUP) {     // B rows 32w + [0,16) = gate j, 32w + [16,32) = up j, same j
       const int j = nt * 64 + 16 * (r >> 5) + (r & 15);
       wr = (r & 16) ? I + j : j;
     } else {
@@ -199,15 +234,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     acc[i][1] = f32x4{0, 0, 0, 0};
   }
   const int groups = (rows + 31) >> 5;
+  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
   switch (groups) {
 #define MOE_CASE(g) \
-    case g: ffn_mainloop<g, BM, STAGES>(smem, a_src, b_src, KD, wave, lane, acc); break;
+    case g: ffn_mainloop<g>(smem, a_src, b_src, A + (size_t)row0 * KD, wexp, KD, wave, lane, acc); break;
     MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
     MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
     default: break;
   }
-  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
 
   // epilogue: lane holds C[16*rb + 4*(lane>>4) + i][col (lane & 15)] of both blocks
 #pragma unroll
@@ -317,11 +352,11 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int row
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
     MOE_LAUNCH("ffn_gateup_bf16", s,
-               ffn_mfma_bf16<kBmBf16, kStagesBf16, true><<<groups * 8 * nt1, kThreads, 0, s>>>(
+               ffn_mfma_bf16<true><<<groups * 8 * nt1, kThreads, 0, s>>>(
                    (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1,
                    (bf16*)hh));
     MOE_LAUNCH("ffn_down_bf16", s,
-               ffn_mfma_bf16<kBmBf16, kStagesBf16, false><<<groups * 8 * nt2, kThreads, 0, s>>>(
+               ffn_mfma_bf16<false><<<groups * 8 * nt2, kThreads, 0, s>>>(
                    (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
                    (bf16*)y_perm));
   } else {

@@ -17,7 +17,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kTokensPerBlock = 32;
+constexpr int kTokensPerBlock = 4;   // one token per wave: many waves in flight
 
 __device__ __forceinline__ uint32_t key_order(float k) {
   if (k != k) return 1u;                    // NaN: above "taken", below every number

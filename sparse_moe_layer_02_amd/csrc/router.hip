@@ -1,14 +1,28 @@
 // Router scores over the whole expert pool (LongCat-Flash Technical Report
-// notes, Key claims [§2.1, §2.4]): logits[t][e] = sum_h x[t][h] * w_router[e][h],
-// fp32 products and fp32 accumulation.
-// LDS-tiled FMA kernel: 64 tokens x 64 experts per block, K step 16, each
-// thread owns a 4x4 patch.  Any T, E, H.
+// notes, Key claims [§2.1, §2.4]): logits[t][e] = sum_h x[t][h] * w_router[e][h]
+// with fp32 router weights and an fp32 result.
+//
+// bf16 activations (H % 64 == 0): matrix cores.  Each fp32 weight w is split
+// exactly into three bf16 planes, w = hi + mid + lo (hi = bf16(w),
+// mid = bf16(w - hi), lo = bf16(w - hi - mid); each difference is exact in
+// fp32 and the remainder is below 2^-24 |w|).  x is bf16, so every product
+// x*hi, x*mid, x*lo is exact in the fp32 accumulator of
+// v_mfma_f32_16x16x32_bf16: three matrix-core passes give fp32-accurate
+// scores at bf16 matrix-core rate instead of the fp32 vector rate.
+//   block: 128 tokens x 64 experts; wave w owns experts [16w, 16w+16) for all
+//   128 tokens; K in 64-element stages; x tile (128 B rows, bf16) and the raw
+//   fp32 weight tile (256 B rows) are filled by global_load_lds_dwordx4 into a
+//   4-stage LDS pipeline; the split happens in registers on the fragment read.
+//   XCD-aware order: the 12 expert tiles of one token tile run on one XCD.
+// fp32 activations (or H % 64 != 0): an LDS-tiled FMA kernel, 64 tokens x 64
+// experts per block, K step 16, a 4x4 patch per thread.  Any T, E, H.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kTM = 64, kTN = 64, kTK = 16, kThreads = 256;
+
 
 template <typename TX>
 __global__ __launch_bounds__(kThreads) void router_fma(const TX* __restrict__ x,
@@ -50,10 +64,132 @@ __global__ __launch_bounds__(kThreads) void router_fma(const TX* __restrict__ x,
     }
 }
 
+// ----------------------------------------------------- matrix-core path --
+constexpr int kRM = 128, kRN = 64, kRK = 64, kRStages = 4;
+constexpr int kAStage = kRM * kRK * 2;          // 16 KB of x
+constexpr int kBStage = kRN * kRK * 4;          // 16 KB of fp32 weights
+constexpr int kRStageBytes = kAStage + kBStage;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// x tile rows: 8 chunks of 16 B, XOR-swizzled by row & 7 as in the expert GEMM.
+__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (row & 7); }
+// weight tile rows: 16 chunks of 16 B (fp32), swizzled by the row's low 4 bits.
+__device__ __forceinline__ int swz16(int row, int chunk) { return chunk ^ (row & 15); }
+
+__device__ __forceinline__ void split3(const f32x4& v0, const f32x4& v1, bf16x8& hi, bf16x8& mid,
+                                       bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float w = i < 4 ? v0[i] : v1[i - 4];
+    const bf16 h = (bf16)w;
+    const float r1 = w - (float)h;
+    const bf16 m = (bf16)r1;
+    const float r2 = r1 - (float)m;
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = (bf16)r2;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void router_mfma(const bf16* __restrict__ x,
+                                                           const float* __restrict__ w, int T,
+                                                           int H, int E, int NTE,
+                                                           float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) char smem[kRStages * kRStageBytes];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NTE) * 8 + xcd;
+  const int nt = slot % NTE;
+  const int m0 = mt * kRM, n0 = nt * kRN;
+  if (m0 >= T) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+
+  // x: 16 instructions of 8 rows per stage (4 per wave)
+  const bf16* a_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave + 4 * q) * 8 + (lane >> 3);
+    a_src[q] = x + (size_t)min(m0 + r, T - 1) * H + swz8(r, lane & 7) * 8;
+  }
+  // weights: 16 instructions of 4 rows (256 B each) per stage (4 per wave)
+  const float* b_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave + 4 * q) * 4 + (lane >> 4);
+    b_src[q] = w + (size_t)min(n0 + r, E - 1) * H + swz16(r, lane & 15) * 4;
+  }
+  auto issue = [&](int stage, int k0) {
+    char* sb = smem + stage * kRStageBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
+                                       (lds_void*)(sb + kAStage + (wave + 4 * q) * 1024), 16, 0,
+                                       0);
+  };
+  constexpr int kLoads = 8;
+  f32x4 acc[kRM / 16];
+#pragma unroll
+  for (int i = 0; i < kRM / 16; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  const int KT = H / kRK;
+#pragma unroll
+  for (int s = 0; s < kRStages - 1; ++s)
+    if (s < KT) issue(s, s * kRK);
+  const int rB = 16 * wave + (lane & 15);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + kRStages - 1 <= KT) wait_vmcnt<kLoads * (kRStages - 2)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + kRStages - 1 < KT) issue((kt + kRStages - 1) % kRStages, (kt + kRStages - 1) * kRK);
+    const char* As = smem + (kt % kRStages) * kRStageBytes;
+    const char* Bs = As + kAStage;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // this lane's 8 k values: k = 32kk + 8(lane/16) .. +8 -> fp32 chunks 2c, 2c+1
+      const int c = kk * 8 + (lane >> 4) * 2;
+      const f32x4 v0 = *(const f32x4*)(Bs + rB * 256 + swz16(rB, c) * 16);
+      const f32x4 v1 = *(const f32x4*)(Bs + rB * 256 + swz16(rB, c + 1) * 16);
+      bf16x8 bh, bm, bl;
+      split3(v0, v1, bh, bm, bl);
+      const int ch = kk * 4 + (lane >> 4);
+#pragma unroll
+      for (int rb = 0; rb < kRM / 16; ++rb) {
+        const int rA = rb * 16 + (lane & 15);
+        const bf16x8 a = *(const bf16x8*)(As + rA * 128 + swz8(rA, ch) * 16);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[rb], 0, 0, 0);
+      }
+    }
+  }
+  const int col = n0 + 16 * wave + (lane & 15);
+  if (col >= E) return;
+#pragma unroll
+  for (int rb = 0; rb < kRM / 16; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = m0 + rb * 16 + 4 * (lane >> 4) + i;
+      if (t < T) logits[(size_t)t * E + col] = acc[rb][i];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int H, int E,
                                 float* logits, hipStream_t s) {
+  if (dtype == MOE_BF16 && H % kRK == 0) {
+    const int nte = (E + kRN - 1) / kRN;
+    const unsigned groups = ceil_div(ceil_div(T, kRM), 8);
+    MOE_LAUNCH("router_logits", s,
+               router_mfma<<<groups * 8 * nte, kThreads, 0, s>>>((const bf16*)x, w, T, H, E, nte,
+                                                                 logits));
+    return hipGetLastError();
+  }
   dim3 grid(ceil_div(E, kTN), ceil_div(T, kTM));
   if (dtype == MOE_BF16)
     MOE_LAUNCH("router_logits", s,
