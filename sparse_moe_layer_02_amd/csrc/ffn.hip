@@ -26,7 +26,9 @@
 //     registers before hh is stored (bf16);
 //   - block -> tile order is XCD-aware: consecutive blocks land on the 8 XCDs
 //     in turn, so all column tiles of one m-tile run on one XCD and re-read
-//     the m-tile's activation rows from that XCD's L2.
+//     the m-tile's activation rows from that XCD's L2; each column tile starts
+//     its K sweep at its own offset so that those re-reads are L2 hits rather
+//     than 32 simultaneous waits on one miss.
 #include "moe_internal.h"
 
 namespace moe {
@@ -130,15 +132,17 @@ struct Pipe {
 template <int G>
 __device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_src,
                                              const bf16* const* b_src, const bf16* a_dummy,
-                                             const bf16* b_dummy, int KD, int wave, int lane,
-                                             f32x4 (&acc)[kBmBf16 / 16][2]) {
+                                             const bf16* b_dummy, int KD, int k_start, int wave,
+                                             int lane, f32x4 (&acc)[kBmBf16 / 16][2]) {
   using P = Pipe<G>;
   constexpr int S = P::S;
   const int KT = KD / kBK;
   auto issue = [&](int kt) {
     char* sb = smem + (kt % S) * P::kStageBytes;
     const bool real = kt < KT;
-    const int k0 = real ? kt * kBK : 0;
+    int ks = kt + k_start;                 // this block's rotated K order
+    ks = ks >= KT ? ks - KT : ks;
+    const int k0 = real ? ks * kBK : 0;
 #pragma unroll
     for (int q = 0; q < P::kAq; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(real ? a_src[q] + k0 : a_dummy),
@@ -180,6 +184,67 @@ __device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_sr
     }
   }
   wait_vmcnt<0>();   // the past-the-end loads land before the block exits
+}
+
+// Full 256-row tiles (experts with many rows: compute-bound).  Same LDS
+// stages as G = 8, but the four waves tile the 256 x 128 block 2 x 2 -- wave
+// (wr, wc) owns rows [128 wr, +128) and weight rows [64 wc, +64) -- so each
+// step reads 96 KB of LDS fragments for 64 MFMAs per wave instead of the
+// 144 KB the column split needs.
+__device__ __forceinline__ void ffn_mainloop_full(char* smem, const bf16* const* a_src,
+                                                  const bf16* const* b_src,
+                                                  const bf16* a_dummy, const bf16* b_dummy,
+                                                  int KD, int k_start, int wave, int lane,
+                                                  f32x4 (&acc)[8][4]) {
+  using P = Pipe<8>;
+  constexpr int S = P::S;
+  const int KT = KD / kBK;
+  auto issue = [&](int kt) {
+    char* sb = smem + (kt % S) * P::kStageBytes;
+    const bool real = kt < KT;
+    int ks = kt + k_start;
+    ks = ks >= KT ? ks - KT : ks;
+    const int k0 = real ? ks * kBK : 0;
+#pragma unroll
+    for (int q = 0; q < P::kAq; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? a_src[q] + k0 : a_dummy),
+                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < P::kBq; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? b_src[q] + k0 : b_dummy),
+                                       (lds_void*)(sb + P::kArows * kRowBytes +
+                                                   (wave + 4 * q) * 1024),
+                                       16, 0, kCachePolicyNT);
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(j);
+  const int wr = wave >> 1, wc = wave & 1;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<P::kLoads * (S - 2)>();
+    lds_barrier();
+    issue(kt + S - 1);
+    const char* As = smem + (kt % S) * P::kStageBytes;
+    const char* Bs = As + P::kArows * kRowBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      bf16x8 b[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int rB = 64 * wc + 16 * cb + (lane & 15);
+        b[cb] = *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, ch) * 16);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb) {
+        const int rA = 128 * wr + rb * 16 + (lane & 15);
+        const bf16x8 a = *(const bf16x8*)(As + rA * kRowBytes + swz(rA, ch) * 16);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], acc[rb][cb], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt<0>();
 }
 
 template <bool GATEUP>
@@ -227,6 +292,47 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     b_src[q] = wexp + (size_t)wr * KD + swz(r, lc) * 8;
   }
 
+  // The column tiles of one m-tile run side by side on one XCD and read the
+  // same activation rows.  Swept in lockstep, every one of them would wait on
+  // the same L2 miss at every step; starting each tile's K sweep at its own
+  // offset (and wrapping around) spreads the first touches out, so the other
+  // tiles hit L2.
+  const int KTt = KD / kBK;
+  const int k_start = (int)(((long long)nt * KTt) / NT) % KTt;
+  const bf16* a_dummy = A + (size_t)row0 * KD;
+  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
+
+  if (rows == BM) {
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    ffn_mainloop_full(smem, a_src, b_src, a_dummy, wexp, KD, k_start, wave, lane, acc);
+    // lane holds C[128 wr + 16 rb + 4 (lane>>4) + i][weight row 64 wc + 16 cb + (lane & 15)]
+    const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 128 * wr + rb * 16 + 4 * (lane >> 4) + i;
+        if (GATEUP) {
+          // weight rows 64 wc + [0,16) gate / [16,32) up of one j block, then the next
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float g = acc[rb][2 * p][i], u = acc[rb][2 * p + 1][i];
+            const float hv = g / (1.0f + expf(-g)) * u;
+            C[(size_t)(row0 + r) * I + nt * 64 + 32 * wc + 16 * p + (lane & 15)] = (bf16)hv;
+          }
+        } else {
+          bf16* crow = C + (size_t)(row0 + r) * H + nt * kBN + 64 * wc + (lane & 15);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) crow[16 * cb] = (bf16)acc[rb][cb][i];
+        }
+      }
+    return;
+  }
+
   f32x4 acc[BM / 16][2];
 #pragma unroll
   for (int i = 0; i < BM / 16; ++i) {
@@ -234,10 +340,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     acc[i][1] = f32x4{0, 0, 0, 0};
   }
   const int groups = (rows + 31) >> 5;
-  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
   switch (groups) {
 #define MOE_CASE(g) \
-    case g: ffn_mainloop<g>(smem, a_src, b_src, A + (size_t)row0 * KD, wexp, KD, wave, lane, acc); break;
+    case g: ffn_mainloop<g>(smem, a_src, b_src, a_dummy, wexp, KD, k_start, wave, lane, acc); \
+      break;
     MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
     MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
