@@ -17,6 +17,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,8 @@ sys.path.insert(0, ROOT)
 import sparse_moe_layer_02_amd as moe  # noqa: E402
 import workload  # noqa: E402
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_traffic.json")
+FFN_SOURCE = os.path.join(ROOT, "sparse_moe_layer_02_amd", "csrc", "ffn.hip")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM MFMA util and HBM GB/s vs peak"
@@ -65,6 +68,22 @@ def algorithmic(cfg, counts, S):
     down_flops = 2.0 * S * I * H
     return dict(active=active, gateup_bytes=gateup_bytes, down_bytes=down_bytes,
                 gateup_flops=gateup_flops, down_flops=down_flops)
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration), or None
+    if they were taken on another workload or another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(FFN_SOURCE, "rb") as f:
+            src = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != src or rec.get("workload") != workload_name:
+        return None
+    return int(rec["bytes_per_launch"])
 
 
 def cpu_baseline(cfg, inp, n_tokens):
@@ -155,7 +174,7 @@ def main():
     k_ms = tot / n_launch
     achieved = alg["gateup_bytes"] / (k_ms * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(cfg.name),
                     kernel=kname, kernel_ms=round(k_ms, 4),
                     algorithmic_bytes=alg["gateup_bytes"],
                     mfma_frac=round(alg["gateup_flops"] / (k_ms * 1e-3) / 1e12
