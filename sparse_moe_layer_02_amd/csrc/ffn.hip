@@ -14,13 +14,13 @@
 //     where the weights (not the MFMA rate) bound the time;
 //   - wave w owns 32 weight rows (two 16-column MFMA blocks) and every row
 //     block of the m-tile; 32-row groups past the expert's rows are skipped;
-//   - K is swept in kBK-element steps staged in LDS by global_load_lds_dwordx4
-//     (16 B per lane, no VGPR staging; weights non-temporal) in one ring as
-//     deep as the 160 KB of LDS allows for the tile's live rows;
-//   - LDS rows hold one step of one row, their 16-byte chunks XOR-swizzled so
+//   - 8 waves: four compute waves (fragment reads + MFMA only) and four
+//     loader waves that stream 64-element K steps by global->LDS DMA into a
+//     ring of 3 to 8 steps;
+//   - LDS rows are 128 B with the 16-byte chunks XOR-swizzled by row & 7 so
 //     that the fragment reads (16 rows x one chunk per 16 lanes) are free of
 //     bank conflicts: timed on gfx950 they run as fast as linear
-//     ds_read_b128 (an unswizzled 128 B-row layout is 2.4x slower);
+//     ds_read_b128 (an unswizzled layout is 2.4x slower);
 //   - gate/up: weight rows are paired so that a lane holds gate column j and
 //     up column j in the same accumulator slot, and silu(g)*u is applied in
 //     registers before hh is stored (bf16);
@@ -34,26 +34,17 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_FFN_BK
-#define MOE_FFN_BK 64
-#endif
-constexpr int kThreads = 256;
-constexpr int kBK = MOE_FFN_BK;                 // k elements per pipeline step
-constexpr int kRowBytes = kBK * 2;              // bytes per LDS row of a step
-constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per LDS row
-constexpr int kRowsPerInstr = 1024 / kRowBytes; // rows one wave-wide 16 B/lane DMA fills
-constexpr int kBN = 128;                        // weight rows per block
+constexpr int kThreads = 256;        // fp32 path and the small kernels
+constexpr int kGemmThreads = 512;    // bf16 GEMM: 4 compute + 4 loader waves
+constexpr int kBK = 64;                 // k elements per pipeline step
+constexpr int kRowBytes = kBK * 2;      // 128 B per LDS row of a step
+constexpr int kBN = 128;                // weight rows per block
 constexpr int kBmBf16 = 256;
 constexpr int kBmF32 = 32;
-static_assert(kBK == 32 || kBK == 64, "K step of 32 or 64 elements");
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Chunk swizzle of an LDS row, chosen so that 16 lanes reading one chunk of
-// 16 consecutive rows (the MFMA fragment read) hit distinct banks.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return kChunks == 8 ? chunk ^ (row & 7) : chunk ^ ((row >> 1) & 3);
-}
+// Chunk swizzle of a 128 B LDS row: 16 lanes reading one 16-byte chunk of 16
+// consecutive rows (the MFMA fragment read) hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 // ------------------------------------------------------------ work list --
 // Rows are clamped to [0, rows_cap) and the list to max_tiles entries, so a
@@ -97,74 +88,123 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
 // -------------------------------------------------------- bf16 MFMA GEMM --
 // GATEUP: A = x_perm [.][H], W = w13 [N][2I][H], C = hh [.][I]   (KD = H, NT = I/64)
 // down  : A = hh     [.][I], W = w2  [N][H][I],  C = y_perm [.][H] (KD = I, NT = H/128)
-//
-// The K loop is instantiated per number G of live 32-row groups of the m-tile
-// (G = ceil(rows / 32)), chosen once per block: each instance is branch-free,
-// loads only the live A rows, issues only the live MFMAs, and lays out as many
-// pipeline stages as fit the 160 KB of LDS for its stage size
-// ((32G + 128) rows x 128 B): 8 stages at G = 1 (decode-sized tiles) down to
-// 3 at G = 8.  The weight tiles in flight per CU -- what sustains HBM
-// bandwidth when the weights dominate -- grow as the activation tile shrinks.
 constexpr int kLdsBytes = 160 * 1024;
+
+// Producer/consumer pipeline, 8 waves (2 per SIMD).
+//   - Waves 4-7 (loaders) only issue loads: global_load_lds_dwordx4, 1 KB
+//     (8 rows x 128 B) per instruction straight into an LDS ring of S steps,
+//     as deep as the 160 KB allow (8 steps at G = 1 down to 3 at G = 8).
+//   - Waves 0-3 (compute) only read fragments from LDS and issue MFMAs.
+// One barrier per step joins all eight.  Under load a 1 KB vector-memory
+// instruction occupies the wave that issues it for ~40-70 cycles; with the
+// roles split those stalls fall on a loader, and the compute wave sharing its
+// SIMD keeps the matrix core busy.  Writing LDS by DMA (rather than through
+// VGPRs and ds_write) keeps the loader's per-step work to issuing loads.
+typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kCachePolicyNT = 2;   // non-temporal: weights are streamed once
 
-// One ring of S steps, each step = the live activation rows plus the 128
-// weight rows over kBK k values, as deep as the 160 KB of LDS allows.
-// Loads complete in issue order, so the wait for step kt also waits for every
-// older load: separate rings for the two operands would not give either one
-// more time in flight.  S is therefore what sets the bytes in flight per CU.
 template <int G>
-struct Pipe {
-  static constexpr int kAq = (32 * G / kRowsPerInstr + 3) / 4;   // A DMA per wave per step
-  static constexpr int kArows = kAq * 4 * kRowsPerInstr;         // >= 32G rows (clamped extras)
-  static constexpr int kBq = kBN / kRowsPerInstr / 4;            // B DMA per wave per step
-  static constexpr int kStageBytes = (kArows + kBN) * kRowBytes;
+struct Ring {
+  static constexpr int kABytes = 32 * G * kRowBytes;   // A tile of one step
+  static constexpr int kStageBytes = kABytes + kBN * kRowBytes;
+  static constexpr int kQa = G;                        // A loads per loader per step
+  static constexpr int kQb = kBN / 8 / 4;              // B loads per loader per step (4)
+  static constexpr int kQ = kQa + kQb;
   static constexpr int kFit = kLdsBytes / kStageBytes;
-  static constexpr int S = kFit > 16 ? 16 : kFit;
-  static constexpr int kLoads = kAq + kBq;
-  static_assert(S >= 3, "pipeline needs three steps");
-  static_assert(kLoads * (S - 2) < 64, "vmcnt range");
-  static_assert(kArows <= kBmBf16, "A source table size");
+  static constexpr int S = kFit > 8 ? 8 : kFit;
+  static_assert(S >= 3, "three steps in the ring");
+  static_assert((S - 2) * kQ < 64, "vmcnt range");
 };
 
-// Every step issues the same loads -- past the end they read one fixed 16-byte
-// line into a slot that is never read -- so every wait count is a constant.
+struct TileSrc {
+  const bf16* a_rows;   // first row of the m-tile (row stride KD)
+  int rows;             // live rows of the m-tile
+  const bf16* w;        // this expert's weight matrix (row stride KD)
+  int nt, I;            // column tile, intermediate size (gate/up pairing)
+  bool gateup;
+};
+
+// Weight row held in row r (0..127) of the block's weight tile.  Gate/up:
+// rows 32w + [0,16) are gate rows j, 32w + [16,32) the up rows of the same j,
+// so that one lane ends up with gate column j and up column j.
+__device__ __forceinline__ int weight_row(const TileSrc& t, int r) {
+  if (t.gateup) {
+    const int j = t.nt * 64 + 16 * (r >> 5) + (r & 15);
+    return (r & 16) ? t.I + j : j;
+  }
+  return t.nt * kBN + r;
+}
+
+// Loader l (0..3) moves 8-row groups l, l+4, ... of both tiles; lane j of an
+// instruction fetches the 16-byte chunk that lands at byte 16 j of the group,
+// i.e. chunk swz(row, j & 7) of row 8 g + (j >> 3).  Every step issues the
+// same loads -- past the end they read one fixed line into a stage no one
+// reads again -- so every wait count is a constant.  The sweep starts at
+// k_start and wraps around.
 template <int G>
-__device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_src,
-                                             const bf16* const* b_src, const bf16* a_dummy,
-                                             const bf16* b_dummy, int KD, int k_start, int wave,
-                                             int lane, f32x4 (&acc)[kBmBf16 / 16][2]) {
-  using P = Pipe<G>;
-  constexpr int S = P::S;
+__device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD, int k_start,
+                                           int l, int lane) {
+  using R = Ring<G>;
+  constexpr int S = R::S, kQ = R::kQ;
   const int KT = KD / kBK;
+  const int lr = lane >> 3, lc = lane & 7;
+  const bf16* src[kQ];
+#pragma unroll
+  for (int i = 0; i < R::kQa; ++i) {
+    const int r = (l + 4 * i) * 8 + lr;        // rows past the tile: clamped (never used)
+    src[i] = t.a_rows + (size_t)min(r, t.rows - 1) * KD + swz(r, lc) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < R::kQb; ++i) {
+    const int r = (l + 4 * i) * 8 + lr;
+    src[R::kQa + i] = t.w + (size_t)weight_row(t, r) * KD + swz(r, lc) * 8;
+  }
   auto issue = [&](int kt) {
-    char* sb = smem + (kt % S) * P::kStageBytes;
+    char* sb = smem + (kt % S) * R::kStageBytes;
     const bool real = kt < KT;
-    int ks = kt + k_start;                 // this block's rotated K order
+    int ks = kt + k_start;
     ks = ks >= KT ? ks - KT : ks;
     const int k0 = real ? ks * kBK : 0;
 #pragma unroll
-    for (int q = 0; q < P::kAq; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(real ? a_src[q] + k0 : a_dummy),
-                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
+    for (int i = 0; i < R::kQa; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? src[i] + k0 : t.w),
+                                       (lds_void*)(sb + (l + 4 * i) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int q = 0; q < P::kBq; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(real ? b_src[q] + k0 : b_dummy),
-                                       (lds_void*)(sb + P::kArows * kRowBytes +
-                                                   (wave + 4 * q) * 1024),
-                                       16, 0, kCachePolicyNT);
+    for (int i = 0; i < R::kQb; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(real ? src[R::kQa + i] + k0 : t.w),
+                                       (lds_void*)(sb + R::kABytes + (l + 4 * i) * 1024), 16,
+                                       0, kCachePolicyNT);
   };
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j) issue(j);
-
-  const int rB0 = 32 * wave + (lane & 15);
-  const int rB1 = rB0 + 16;
+  for (int kt = 0; kt < S - 1; ++kt) issue(kt);
   for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt<P::kLoads * (S - 2)>();   // step kt has landed (this wave's loads)
-    lds_barrier();                       // ... and every wave's; slot kt-1 is free
-    issue(kt + S - 1);
-    const char* As = smem + (kt % S) * P::kStageBytes;
-    const char* Bs = As + P::kArows * kRowBytes;
+    wait_vmcnt<(S - 2) * kQ>();   // step kt has landed (in-order completion)
+    lds_barrier();                // publish step kt; every wave is done with step kt - 1
+    issue(kt + S - 1);            // into the stage step kt - 1 used
+  }
+  wait_vmcnt<0>();   // the past-the-end loads land before the block exits
+}
+
+// The compute waves' K sweep: step kt reads stage kt % S.
+template <int G, class Compute>
+__device__ __forceinline__ void ffn_consumer(char* smem, int KD, Compute&& compute) {
+  using R = Ring<G>;
+  const int KT = KD / kBK;
+  for (int kt = 0; kt < KT; ++kt) {
+    lds_barrier();
+    const char* As = smem + (kt % R::S) * R::kStageBytes;
+    compute(As, As + R::kABytes);
+  }
+}
+
+// Partial tiles: wave w owns weight rows [32w, 32w+32) (two 16-column MFMA
+// blocks) and all 32G live rows.
+template <int G>
+struct ColumnSplit {
+  f32x4 (&acc)[kBmBf16 / 16][2];
+  int wave, lane;
+  __device__ __forceinline__ void operator()(const char* As, const char* Bs) const {
+    const int rB0 = 32 * wave + (lane & 15);
+    const int rB1 = rB0 + 16;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
@@ -183,48 +223,17 @@ __device__ __forceinline__ void ffn_mainloop(char* smem, const bf16* const* a_sr
       }
     }
   }
-  wait_vmcnt<0>();   // the past-the-end loads land before the block exits
-}
+};
 
-// Full 256-row tiles (experts with many rows: compute-bound).  Same LDS
-// stages as G = 8, but the four waves tile the 256 x 128 block 2 x 2 -- wave
-// (wr, wc) owns rows [128 wr, +128) and weight rows [64 wc, +64) -- so each
-// step reads 96 KB of LDS fragments for 64 MFMAs per wave instead of the
-// 144 KB the column split needs.
-__device__ __forceinline__ void ffn_mainloop_full(char* smem, const bf16* const* a_src,
-                                                  const bf16* const* b_src,
-                                                  const bf16* a_dummy, const bf16* b_dummy,
-                                                  int KD, int k_start, int wave, int lane,
-                                                  f32x4 (&acc)[8][4]) {
-  using P = Pipe<8>;
-  constexpr int S = P::S;
-  const int KT = KD / kBK;
-  auto issue = [&](int kt) {
-    char* sb = smem + (kt % S) * P::kStageBytes;
-    const bool real = kt < KT;
-    int ks = kt + k_start;
-    ks = ks >= KT ? ks - KT : ks;
-    const int k0 = real ? ks * kBK : 0;
-#pragma unroll
-    for (int q = 0; q < P::kAq; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(real ? a_src[q] + k0 : a_dummy),
-                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < P::kBq; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(real ? b_src[q] + k0 : b_dummy),
-                                       (lds_void*)(sb + P::kArows * kRowBytes +
-                                                   (wave + 4 * q) * 1024),
-                                       16, 0, kCachePolicyNT);
-  };
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j) issue(j);
-  const int wr = wave >> 1, wc = wave & 1;
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt<P::kLoads * (S - 2)>();
-    lds_barrier();
-    issue(kt + S - 1);
-    const char* As = smem + (kt % S) * P::kStageBytes;
-    const char* Bs = As + P::kArows * kRowBytes;
+// Full 256-row tiles (experts with many rows: compute-bound): the four waves
+// tile the 256 x 128 block 2 x 2 -- wave (wr, wc) owns rows [128 wr, +128)
+// and weight rows [64 wc, +64) -- reading 96 KB of LDS fragments per step for
+// 64 MFMAs per wave instead of the 144 KB the column split needs.
+struct Quadrant {
+  f32x4 (&acc)[8][4];
+  int wave, lane;
+  __device__ __forceinline__ void operator()(const char* As, const char* Bs) const {
+    const int wr = wave >> 1, wc = wave & 1;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
@@ -244,14 +253,14 @@ __device__ __forceinline__ void ffn_mainloop_full(char* smem, const bf16* const*
       }
     }
   }
-  wait_vmcnt<0>();
-}
+};
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const int4* __restrict__ tiles,
     const int* __restrict__ ntiles, int KD, int I, int H, int NT, bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
+  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int b = blockIdx.x;
@@ -261,46 +270,31 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
   if (mt >= *ntiles) return;
   const int4 tile = tiles[mt];
   const int e = tile.x, row0 = tile.y, rows = tile.z;
-
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int lr = lane / kChunks;   // row within the rows one DMA instruction fills
-  const int lc = lane % kChunks;   // 16-byte slot within the LDS row
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
 
-  // global source of this lane's 16-byte loads (k offset added per step);
-  // rows past the tile are clamped to its last row (never used)
-  constexpr int kAsrc = BM / kRowsPerInstr / 4;
-  const bf16* a_src[kAsrc];
-#pragma unroll
-  for (int q = 0; q < kAsrc; ++q) {
-    const int r = (wave + 4 * q) * kRowsPerInstr + lr;
-    a_src[q] = A + (size_t)(row0 + min(r, rows - 1)) * KD + swz(r, lc) * 8;
-  }
   const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
-  const bf16* wexp = W + (size_t)e * wrows * KD;
-  const bf16* b_src[kBN / kRowsPerInstr / 4];
-#pragma unroll
-  for (int q = 0; q < kBN / kRowsPerInstr / 4; ++q) {
-    const int r = (wave + 4 * q) * kRowsPerInstr + lr;
-    int wr;
-    if (GATEUP) {     // B rows 32w + [0,16) = gate j, 32w + [16,32) = up j, same j
-      const int j = nt * 64 + 16 * (r >> 5) + (r & 15);
-      wr = (r & 16) ? I + j : j;
-    } else {
-      wr = nt * kBN + r;
-    }
-    b_src[q] = wexp + (size_t)wr * KD + swz(r, lc) * 8;
-  }
-
+  const TileSrc src{A + (size_t)row0 * KD, rows, W + (size_t)e * wrows * KD, nt, I, GATEUP};
   // The column tiles of one m-tile run side by side on one XCD and read the
   // same activation rows.  Swept in lockstep, every one of them would wait on
   // the same L2 miss at every step; starting each tile's K sweep at its own
   // offset (and wrapping around) spreads the first touches out, so the other
   // tiles hit L2.
-  const int KTt = KD / kBK;
-  const int k_start = (int)(((long long)nt * KTt) / NT) % KTt;
-  const bf16* a_dummy = A + (size_t)row0 * KD;
-  static_assert(BM == 256, "instances cover 8 groups of 32 rows");
+  const int KT = KD / kBK;
+  const int k_start = (int)(((long long)nt * KT) / NT) % KT;
+
+  const int groups = (rows + 31) >> 5;
+  if (wave >= 4) {   // loader waves
+    switch (groups) {
+#define MOE_CASE(g) \
+      case g: ffn_loader<g>(smem, src, KD, k_start, wave - 4, lane); break;
+      MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
+      MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+#undef MOE_CASE
+      default: break;
+    }
+    return;
+  }
 
   if (rows == BM) {
     f32x4 acc[8][4];
@@ -308,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-    ffn_mainloop_full(smem, a_src, b_src, a_dummy, wexp, KD, k_start, wave, lane, acc);
+    ffn_consumer<8>(smem, KD, Quadrant{acc, wave, lane});
     // lane holds C[128 wr + 16 rb + 4 (lane>>4) + i][weight row 64 wc + 16 cb + (lane & 15)]
     const int wr = wave >> 1, wc = wave & 1;
 #pragma unroll
@@ -339,11 +333,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_mfma_bf16(
     acc[i][0] = f32x4{0, 0, 0, 0};
     acc[i][1] = f32x4{0, 0, 0, 0};
   }
-  const int groups = (rows + 31) >> 5;
+  // K loop instantiated per number of live 32-row groups: branch-free, only
+  // the live rows are loaded and only their MFMAs issued.
   switch (groups) {
-#define MOE_CASE(g) \
-    case g: ffn_mainloop<g>(smem, a_src, b_src, a_dummy, wexp, KD, k_start, wave, lane, acc); \
-      break;
+#define MOE_CASE(g)                                                      \
+    case g: ffn_consumer<g>(smem, KD, ColumnSplit<g>{acc, wave, lane}); break;
     MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
     MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
@@ -458,11 +452,11 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int row
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
     MOE_LAUNCH("ffn_gateup_bf16", s,
-               ffn_mfma_bf16<true><<<groups * 8 * nt1, kThreads, 0, s>>>(
+               ffn_mfma_bf16<true><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
                    (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1,
                    (bf16*)hh));
     MOE_LAUNCH("ffn_down_bf16", s,
-               ffn_mfma_bf16<false><<<groups * 8 * nt2, kThreads, 0, s>>>(
+               ffn_mfma_bf16<false><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
                    (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
                    (bf16*)y_perm));
   } else {
