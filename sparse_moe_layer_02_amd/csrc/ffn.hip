@@ -24,6 +24,8 @@
 //   - gate/up: weight rows are paired so that a lane holds gate column j and
 //     up column j in the same accumulator slot, and silu(g)*u is applied in
 //     registers before hh is stored (bf16);
+//   - the output tile is staged in LDS and stored 16 bytes per lane (whole
+//     128-byte lines), not one 2-byte value per lane per instruction;
 //   - block -> tile order is XCD-aware: consecutive blocks land on the 8 XCDs
 //     in turn, so all column tiles of one m-tile run on one XCD and re-read
 //     the m-tile's activation rows from that XCD's L2; each column tile starts
@@ -255,6 +257,35 @@ struct Quadrant {
   }
 };
 
+// Epilogue through LDS.  Written straight from the accumulators, the output
+// takes one 2-byte value per lane per store instruction (32-64 instructions
+// per wave), and each of those waits its turn in the CU's memory pipeline
+// behind the other blocks' streams -- on the full-scale layer that cost more
+// than the K loop's own stalls.  Instead the values go to an LDS tile
+// [rows][NC] (row pitch NC * 2 + 16 bytes), and the tile leaves with
+// 16 bytes per lane, whole 128-byte lines of output per instruction.
+template <int NC>
+struct OutTile {
+  static constexpr int kPitch = NC * 2 + 16;
+  static constexpr int kChunks = NC / 8;        // 16-byte chunks per row
+  char* t;
+  __device__ __forceinline__ void put(int r, int c, float v) const {
+    *(bf16*)(t + r * kPitch + c * 2) = (bf16)v;
+  }
+  // tid: 0..255 over the four compute waves
+  __device__ __forceinline__ void flush(bf16* __restrict__ C, int ld, int row0, int col0,
+                                        int rows, int tid) const {
+    for (int j = tid; j < rows * kChunks; j += 256) {
+      const int r = j / kChunks, c = j - r * kChunks;
+      const i32x4 v = *(const i32x4*)(t + r * kPitch + c * 16);
+      *(i32x4*)(C + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
+    }
+  }
+};
+static_assert(kBmBf16 * OutTile<kBN>::kPitch <= kLdsBytes, "output tile fits LDS");
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 template <bool GATEUP>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const int4* __restrict__ tiles,
@@ -293,9 +324,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 #undef MOE_CASE
       default: break;
     }
+    // Two more barriers, matching the compute waves': the LDS is free for the
+    // output tile (every load has landed), then the tile is written.
+    lds_barrier();
+    lds_barrier();
     return;
   }
 
+  // Output tile: gate/up 64 hh columns, down 128 y columns of this column tile.
+  constexpr int NC = GATEUP ? kBN / 2 : kBN;
+  const OutTile<NC> out{smem};
+  const int c = lane & 15, q = lane >> 4;
   if (rows == BM) {
     f32x4 acc[8][4];
 #pragma unroll
@@ -303,66 +342,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     ffn_consumer<8>(smem, KD, Quadrant{acc, wave, lane});
-    // lane holds C[128 wr + 16 rb + 4 (lane>>4) + i][weight row 64 wc + 16 cb + (lane & 15)]
+    lds_barrier();   // loads landed, fragments read: the LDS is free
+    // lane holds C[128 wr + 16 rb + 4 q + i][weight row 64 wc + 16 cb + c]
     const int wr = wave >> 1, wc = wave & 1;
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 128 * wr + rb * 16 + 4 * (lane >> 4) + i;
+        const int r = 128 * wr + rb * 16 + 4 * q + i;
         if (GATEUP) {
-          // weight rows 64 wc + [0,16) gate / [16,32) up of one j block, then the next
+          // weight rows 64 wc + [0,16) gate / [16,32) up of one column block, then the next
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const float g = acc[rb][2 * p][i], u = acc[rb][2 * p + 1][i];
-            const float hv = g / (1.0f + expf(-g)) * u;
-            C[(size_t)(row0 + r) * I + nt * 64 + 32 * wc + 16 * p + (lane & 15)] = (bf16)hv;
-          }
+          for (int p = 0; p < 2; ++p)
+            out.put(r, 32 * wc + 16 * p + c, silu_mul(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]));
         } else {
-          bf16* crow = C + (size_t)(row0 + r) * H + nt * kBN + 64 * wc + (lane & 15);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) crow[16 * cb] = (bf16)acc[rb][cb][i];
+          for (int cb = 0; cb < 4; ++cb) out.put(r, 64 * wc + 16 * cb + c, acc[rb][cb][i]);
         }
       }
-    return;
-  }
-
-  f32x4 acc[BM / 16][2];
+  } else {
+    f32x4 acc[BM / 16][2];
 #pragma unroll
-  for (int i = 0; i < BM / 16; ++i) {
-    acc[i][0] = f32x4{0, 0, 0, 0};
-    acc[i][1] = f32x4{0, 0, 0, 0};
-  }
-  // K loop instantiated per number of live 32-row groups: branch-free, only
-  // the live rows are loaded and only their MFMAs issued.
-  switch (groups) {
+    for (int i = 0; i < BM / 16; ++i) {
+      acc[i][0] = f32x4{0, 0, 0, 0};
+      acc[i][1] = f32x4{0, 0, 0, 0};
+    }
+    // K loop instantiated per number of live 32-row groups: branch-free, only
+    // the live rows are loaded and only their MFMAs issued.
+    switch (groups) {
 #define MOE_CASE(g)                                                      \
-    case g: ffn_consumer<g>(smem, KD, ColumnSplit<g>{acc, wave, lane}); break;
-    MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
-    MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+      case g: ffn_consumer<g>(smem, KD, ColumnSplit<g>{acc, wave, lane}); break;
+      MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
+      MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
-    default: break;
-  }
-
-  // epilogue: lane holds C[16*rb + 4*(lane>>4) + i][col (lane & 15)] of both blocks
+      default: break;
+    }
+    lds_barrier();   // loads landed, fragments read: the LDS is free
+    // lane holds C[16 rb + 4 q + i][weight row 32 wave + 16 cb + c]
 #pragma unroll
-  for (int rb = 0; rb < BM / 16; ++rb) {
-    if (rb * 16 >= rows) continue;
+    for (int rb = 0; rb < BM / 16; ++rb) {
+      if (rb * 16 >= rows) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + 4 * (lane >> 4) + i;
-      if (r >= rows) continue;
-      if (GATEUP) {
-        const float g = acc[rb][0][i], u = acc[rb][1][i];
-        const float hv = g / (1.0f + expf(-g)) * u;
-        C[(size_t)(row0 + r) * I + nt * 64 + 16 * wave + (lane & 15)] = (bf16)hv;
-      } else {
-        bf16* crow = C + (size_t)(row0 + r) * H + nt * kBN + 32 * wave + (lane & 15);
-        crow[0] = (bf16)acc[rb][0][i];
-        crow[16] = (bf16)acc[rb][1][i];
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * q + i;
+        if (GATEUP) {
+          out.put(r, 16 * wave + c, silu_mul(acc[rb][0][i], acc[rb][1][i]));
+        } else {
+          out.put(r, 32 * wave + c, acc[rb][0][i]);
+          out.put(r, 32 * wave + 16 + c, acc[rb][1][i]);
+        }
       }
     }
   }
+  lds_barrier();   // the four compute waves' values are in the tile
+  out.flush(C, GATEUP ? I : H, row0, nt * NC, rows, threadIdx.x);
 }
 
 // ------------------------------------------------------------ fp32 path --
