@@ -66,6 +66,9 @@ def _load():
             lib.oracle_zero_experts.restype = None
             lib.oracle_combine.argtypes = [P, P, P, P, ctypes.c_double, P, I, I, I, I, P]
             lib.oracle_combine.restype = None
+            D = ctypes.c_double
+            lib.oracle_bias_update.argtypes = [P, I, I, D, D, D, D, P, P, P]
+            lib.oracle_bias_update.restype = None
             _lib = lib
     return _lib
 
@@ -231,6 +234,24 @@ def combine(y_perm: np.ndarray, slot_row: np.ndarray, idx: np.ndarray, gate: np.
     lib.oracle_combine(_p(y_perm), _p(slot_row), _p(idx), _p(gate), float(scale), _p(y_acc),
                        T, H, K, n_ffn, _p(out))
     return out
+
+
+def bias_update(counts: np.ndarray, T: int, n_ffn: int, target: float, kp: float, ki: float,
+                kd: float, bias: np.ndarray, integral: np.ndarray, prev: np.ndarray):
+    """One update of the FFN experts' selection bias from a batch's routing
+    counts (see ``oracle_bias_update``).  Returns new (bias, integral, prev)
+    as fp64 arrays; bias keeps its length, entries >= n_ffn unchanged."""
+    lib = _load()
+    counts = _c(counts, np.int32)
+    bias = np.array(bias, np.float64)
+    integral = np.array(integral, np.float64)
+    prev = np.array(prev, np.float64)
+    if counts.shape[0] < n_ffn or bias.shape[0] < n_ffn or integral.shape[0] < n_ffn \
+            or prev.shape[0] < n_ffn:
+        raise ValueError("counts, bias, integral and prev need n_ffn entries")
+    lib.oracle_bias_update(_p(counts), int(T), int(n_ffn), float(target), float(kp), float(ki),
+                           float(kd), _p(bias), _p(integral), _p(prev))
+    return bias, integral, prev
 
 
 # ------------------------------------------------------------ whole layer ----

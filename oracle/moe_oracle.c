@@ -228,3 +228,30 @@ void oracle_combine(const double *y_perm, const int32_t *slot_row,
         }
     }
 }
+
+/* ---- bias controller -----------------------------------------------------
+ * Per FFN expert i (identity experts' biases are never touched -- Technical
+ * Report notes, Key claims [§2.1.1, §2.1.2]: "the PID update excludes
+ * zero-computation experts"):
+ *   err_i      = target / n_ffn - counts[i] / T
+ *                (the expert's routing frequency below its share of the
+ *                target number of activated FFN experts per token; summed
+ *                over i it is target - FFN picks per token)
+ *   integral_i = integral_i + err_i
+ *   bias_i     = bias_i + kp * err_i + ki * integral_i + kd * (err_i - prev_i)
+ *   prev_i     = err_i
+ * The report's controller adjusts each FFN expert's bias from token-routing
+ * frequency, refining the aux-loss-free update (bias += step * sign(error)),
+ * to hold the average number of activated FFN experts at a target
+ * (Key claims [§2.1.1], Method).  The error, the increment form and the gains
+ * are not on the pages: this is the plainest reading (the aux-loss-free
+ * update with sign(err) replaced by a PID of err).  State in fp64. */
+void oracle_bias_update(const int32_t *counts, int T, int n_ffn, double target, double kp,
+                        double ki, double kd, double *bias, double *integral, double *prev) {
+    for (int i = 0; i < n_ffn; ++i) {
+        double err = target / (double)n_ffn - (double)counts[i] / (double)T;
+        integral[i] = integral[i] + err;
+        bias[i] = bias[i] + kp * err + ki * integral[i] + kd * (err - prev[i]);
+        prev[i] = err;
+    }
+}

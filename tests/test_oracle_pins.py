@@ -353,3 +353,103 @@ def test_ffn_share_matches_the_pages_average():
     idx, _, _ = oracle.route(l32, b, cfg.K)
     share = (idx < cfg.N).mean()
     assert abs(share - 0.662) < 0.025, share
+
+
+# --------------------------------------------------------- bias controller --
+
+def _counts_case():
+    # 6 FFN experts + 3 identity experts; T = 40 tokens, K = 3 picks each
+    counts = np.array([12, 30, 20, 0, 8, 10, 15, 10, 15], np.int32)
+    assert counts.sum() == 40 * 3
+    return counts, 40, 6
+
+
+def test_bias_update_errors_sum_to_the_activation_gap():
+    # summed over FFN experts the proportional step is kp * (target - FFN picks per token)
+    counts, T, N = _counts_case()
+    for target in (1.0, 2.0, 2.5):
+        b, _, _ = oracle.bias_update(counts, T, N, target, 0.7, 0.0, 0.0, np.zeros(9),
+                                     np.zeros(N), np.zeros(N))
+        assert b[:N].sum() == pytest.approx(0.7 * (target - counts[:N].sum() / T), abs=1e-12)
+
+
+def test_bias_update_pushes_against_the_load():
+    counts, T, N = _counts_case()
+    target = counts[:N].sum() / T          # on target in total: only the balance moves
+    b, _, _ = oracle.bias_update(counts, T, N, target, 1.0, 0.0, 0.0, np.zeros(9), np.zeros(N),
+                                 np.zeros(N))
+    share = target / N
+    load = counts[:N] / T
+    assert np.all(np.sign(b[:N]) == -np.sign(load - share))   # overloaded down, idle up
+    assert np.argmin(b[:N]) == np.argmax(load) and np.argmax(b[:N]) == np.argmin(load)
+
+
+def test_bias_update_fixed_point_and_identity_experts_untouched():
+    T, N = 64, 8
+    counts = np.array([24] * N + [17, 99, 0], np.int32)       # every FFN expert at 24 / 64
+    b0 = _rng(3).uniform(-0.3, 0.3, N + 3)
+    b, integ, prev = oracle.bias_update(counts, T, N, 24 * N / T, 1.3, 0.4, 0.9, b0,
+                                        np.zeros(N), np.zeros(N))
+    np.testing.assert_array_equal(b, b0)                       # on target: nothing moves
+    np.testing.assert_array_equal(integ, 0)
+    counts[:N] = [40, 0, 30, 10, 20, 24, 24, 44]
+    b, _, _ = oracle.bias_update(counts, T, N, 2.7, 1.3, 0.4, 0.9, b0, np.zeros(N), np.zeros(N))
+    np.testing.assert_array_equal(b[N:], b0[N:])              # identity experts: never updated
+    assert np.all(b[:N] != b0[:N])
+
+
+def test_bias_update_integral_and_derivative_terms():
+    counts, T, N = _counts_case()
+    z = np.zeros(N)
+    # integral only, constant counts: the n-th step is n times the first
+    b, i, p = oracle.bias_update(counts, T, N, 2.0, 0.0, 0.3, 0.0, np.zeros(9), z, z)
+    d1 = b[:N].copy()
+    steps = [d1]
+    for _ in range(3):
+        nb, i, p = oracle.bias_update(counts, T, N, 2.0, 0.0, 0.3, 0.0, b, i, p)
+        steps.append(nb[:N] - b[:N])
+        b = nb
+    for n, d in enumerate(steps, 1):
+        np.testing.assert_allclose(d, n * d1, rtol=1e-12, atol=1e-15)
+    # derivative only, constant counts: a kick on the first step, nothing after
+    b, i, p = oracle.bias_update(counts, T, N, 2.0, 0.0, 0.0, 0.5, np.zeros(9), z, z)
+    nb, _, _ = oracle.bias_update(counts, T, N, 2.0, 0.0, 0.0, 0.5, b, i, p)
+    np.testing.assert_array_equal(nb, b)
+    assert np.abs(b[:N]).max() > 0
+
+
+@pytest.mark.parametrize("target", [2.0, 3.0])
+def test_bias_controller_holds_the_activated_ffn_count(target):
+    # Closed loop on the oracle's own router (tiny layer, K = 4 of 16 + 8):
+    # the FFN picks per token settle at the target from either side of the
+    # uncontrolled share (~2.59) and the FFN experts' loads even out.
+    cfg = workload.CONFIGS["tiny_fp32"]
+    x = workload.make_x(cfg).numpy()
+    l32 = oracle.router_logits(x, workload.make_router(cfg).numpy()).astype(np.float32)
+    T, N, K = cfg.T, cfg.N, cfg.K
+    bias = workload.make_bias(cfg).numpy().astype(np.float64)
+    integ, prev = np.zeros(N), np.zeros(N)
+    hist = []
+    for _ in range(200):
+        _, _, counts = oracle.route(l32, bias.astype(np.float32), K)
+        hist.append(counts[:N].sum() / T)
+        bias, integ, prev = oracle.bias_update(counts, T, N, target, 1.0, 0.05, 0.2, bias, integ,
+                                               prev)
+    h = np.array(hist)
+    assert abs(h[0] - 2.59) < 0.05
+    assert abs(h[-50:].mean() - target) < 0.01 and np.abs(h[-50:] - target).max() < 0.05
+    load = counts[:N] / T
+    assert load.std() / load.mean() < 0.1
+
+
+def test_bias_update_derivative_opposes_a_rising_load():
+    # kd only: from a balanced batch (no error, no kick) to one where expert 0
+    # takes more tokens and expert 1 fewer: expert 0's bias must fall, 1's rise.
+    T, N = 32, 4
+    z = np.zeros(N)
+    bal = np.array([16, 16, 16, 16, 32], np.int32)
+    b, i, p = oracle.bias_update(bal, T, N, 2.0, 0.0, 0.0, 0.8, np.zeros(5), z, z)
+    np.testing.assert_array_equal(b, 0)
+    moved = np.array([24, 8, 16, 16, 32], np.int32)
+    nb, _, _ = oracle.bias_update(moved, T, N, 2.0, 0.0, 0.0, 0.8, b, i, p)
+    assert nb[0] < 0 < nb[1] and nb[2] == nb[3] == 0
