@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=96,
                    help="tokens of the oracle's CPU sample (0 = skip)")
     p.add_argument("--kernels", action="store_true", help="also print the per-kernel table")
+    p.add_argument("--bias-controller", type=float, default=0.0, metavar="TARGET",
+                   help="also run one bias-controller update per step (moe_bias_update, "
+                        "FFN experts per token held at TARGET; gains 1.0/0.05/0.2)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -144,9 +147,16 @@ def main():
         torch.cuda.synchronize(dev)
         del src, dst
 
+    bias = inp["bias"].clone()
+    if args.bias_controller > 0:
+        integral = torch.zeros(cfg.N, dtype=torch.float32, device=dev)
+        prev_err = torch.zeros(cfg.N, dtype=torch.float32, device=dev)
+
     def step():
-        moe.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K,
-                    cfg.scale, buf)
+        moe.forward(inp["x"], inp["w_router"], bias, inp["w13"], inp["w2"], cfg.K, cfg.scale, buf)
+        if args.bias_controller > 0:
+            moe.moe_bias_update(buf["counts"], cfg.T, cfg.N, args.bias_controller, 1.0, 0.05, 0.2,
+                                bias, integral, prev_err)
 
     for _ in range(args.warmup):
         step()
@@ -194,7 +204,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, N(0,sigma) weights; no checkpoint)",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "ffn_experts": cfg.N,
+        "config": {"workload": cfg.name + ("+bias_controller" if args.bias_controller > 0 else ""),
+                   "tokens": cfg.T, "hidden": cfg.H, "ffn_experts": cfg.N,
                    "zero_experts": cfg.Z, "intermediate": cfg.I, "top_k": cfg.K,
                    "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"]},
         "roofline": roofline,

@@ -138,6 +138,26 @@ moe_status moe_combine(const void *y_perm, int dtype, const int32_t *slot_row,
                        const float *topk_gate, float ffn_scale, const float *y_acc,
                        int T, int H, int K, void *y, void *stream);
 
+/* Bias controller (Technical Report notes, Key claims [§2.1.1, §2.1.2] and
+ * Method: each FFN expert's selection bias is adjusted from token-routing
+ * frequency by a PID controller so that the average number of activated FFN
+ * experts per token holds a target; zero-computation experts are excluded).
+ * One update from a batch's counts (as written by moe_route for T tokens):
+ * for i in 0..n_ffn-1,
+ *   err_i       = target / n_ffn - counts[i] / T
+ *   integral[i] = integral[i] + err_i
+ *   bias[i]     = bias[i] + kp * err_i + ki * integral[i] + kd * (err_i - prev_err[i])
+ *   prev_err[i] = err_i
+ * bias[n_ffn..E-1] (the zero-computation experts) is not read or written.
+ * target: FFN experts activated per token (0 < target <= K in practice).
+ * counts: [>= n_ffn] int32; bias: [>= n_ffn] fp32 (the array moe_route
+ * reads); integral, prev_err: [n_ffn] fp32 controller state, owned by the
+ * caller, zero before the first update.  fp32 arithmetic.
+ * MOE_ERR_SHAPE: T < 1, n_ffn outside 1..4096, or a non-finite target or gain. */
+moe_status moe_bias_update(const int32_t *counts, int T, int n_ffn, float target, float kp,
+                           float ki, float kd, float *bias, float *integral, float *prev_err,
+                           void *stream);
+
 /* Diagnostics (not part of the layer): opt-in per-kernel timing.  While
  * enabled, each kernel the calls above enqueue is bracketed by two HIP events
  * recorded on its stream.  moe_profile_enable(1) starts a new session (the

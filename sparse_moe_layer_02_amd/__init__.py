@@ -37,6 +37,8 @@ _SIGS = {
     "moe_expert_ffn": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
+    "moe_bias_update": ([_P, _I, _I, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                         ctypes.c_float, _P, _P, _P, _P], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_profile_enable": ([_I], _I),
     "moe_profile_summary": ([ctypes.c_char_p, ctypes.c_size_t], _I),
@@ -182,6 +184,19 @@ def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
     _check("moe_combine", lib().moe_combine(
         _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
+
+
+def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_err):
+    """One PID update of the FFN experts' selection bias from a batch's counts."""
+    _dev(counts, bias, integral, prev_err)
+    _want(counts, torch.int32, "counts")
+    for t, n in ((bias, "bias"), (integral, "integral"), (prev_err, "prev_err")):
+        _want(t, torch.float32, n)
+    assert counts.numel() >= n_ffn and bias.numel() >= n_ffn
+    assert integral.numel() >= n_ffn and prev_err.numel() >= n_ffn
+    _check("moe_bias_update", lib().moe_bias_update(
+        _ptr(counts), int(T), int(n_ffn), float(target), float(kp), float(ki), float(kd),
+        _ptr(bias), _ptr(integral), _ptr(prev_err), _stream(bias)))
 
 
 # ------------------------------------------------------------ diagnostics --

@@ -14,6 +14,7 @@ constexpr int kMaxKCombine = 1024;
 inline bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline bool fits_i32(long long v) { return v >= 0 && v < (1ll << 31); }
+inline bool finite(float v) { return v == v && v - v == 0.0f; }
 
 inline moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
@@ -128,6 +129,19 @@ moe_status moe_combine(const void* y_perm, int dtype, const int32_t* slot_row,
     return MOE_ERR_ALIGN;
   return launched(launch_combine(y_perm, dtype, slot_row, topk_gate, ffn_scale, y_acc, T, H, K, y,
                                  (hipStream_t)stream));
+}
+
+moe_status moe_bias_update(const int32_t* counts, int T, int n_ffn, float target, float kp,
+                           float ki, float kd, float* bias, float* integral, float* prev_err,
+                           void* stream) {
+  if (!counts || !bias || !integral || !prev_err) return MOE_ERR_NULL;
+  if (T < 1 || n_ffn < 1 || n_ffn > kMaxFfn || !finite(target) || !finite(kp) || !finite(ki) ||
+      !finite(kd))
+    return MOE_ERR_SHAPE;
+  if (!aligned(counts, 4) || !aligned(bias, 4) || !aligned(integral, 4) || !aligned(prev_err, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral,
+                                     prev_err, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -78,5 +78,8 @@ hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, con
 hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row,
                           const float* gate, float scale, const float* y_acc, int T, int H,
                           int K, void* y, hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, int T, int n_ffn, float target, float kp,
+                              float ki, float kd, float* bias, float* integral, float* prev,
+                              hipStream_t s);
 
 }  // namespace moe

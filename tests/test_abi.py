@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -123,3 +123,23 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.moe_router_logits(x, torch.zeros((8, 64)), torch.zeros((4, 8)))
+
+
+def test_bias_update_validation():
+    f = moe.lib().moe_bias_update
+    F = ctypes.c_float
+    args = [FAKE, 64, 16, F(2.0), F(1.0), F(0.05), F(0.2), FAKE, FAKE, FAKE, None]
+    a = list(args); a[7] = None
+    assert f(*a) == NULL
+    a = list(args); a[1] = 0                      # no tokens
+    assert f(*a) == SHAPE
+    a = list(args); a[2] = 0                      # no FFN experts
+    assert f(*a) == SHAPE
+    a = list(args); a[2] = 5000                   # beyond 4096
+    assert f(*a) == SHAPE
+    a = list(args); a[3] = F(float("nan"))        # non-finite target
+    assert f(*a) == SHAPE
+    a = list(args); a[6] = F(float("inf"))        # non-finite gain
+    assert f(*a) == SHAPE
+    a = list(args); a[8] = P(0x10002)
+    assert f(*a) == ALIGN
