@@ -176,3 +176,24 @@ def test_rows_past_the_grouped_rows_are_untouched():
     assert (host(buf["x_perm"][S:]) == 123.0).all()
     assert (host(buf["y_perm"][S:]) == -7.0).all()
     assert (host(buf["row_src"][S:]) == -5).all()
+
+
+@pytest.mark.parametrize("T,H,I,heavy,boost", [(4000, 256, 128, (0, 1), 1.5),
+                                               (2000, 640, 320, (2,), 6.0)])
+def test_heavy_experts_many_m_tiles(T, H, I, heavy, boost):
+    # Experts with 8-16 m-tiles of 256 rows next to light ones.  Case 1: two
+    # experts with ~3000 rows each (12 m-tiles, a ragged last one) and 2
+    # column tiles per GEMM.  Case 2: one expert with 2000 rows (8 m-tiles,
+    # the last of 208 rows) and 5 column tiles.
+    N, Z, K = 6, 2, len(heavy) if len(heavy) > 1 else 2
+    cfg = workload.MoEConfig("heavy", T=T, H=H, N=N, Z=Z, I=I, K=K, dtype="bf16", sigma_w=0.05,
+                             bias_lo=0.0, bias_hi=0.0, scale=1.25)
+    bias = np.zeros(N + Z, np.float32)
+    bias[list(heavy)] = boost
+    inp, buf = _run(cfg, bias)
+    counts = host(buf["counts"])[:N]
+    print("rows per FFN expert", counts.tolist(), flush=True)
+    assert all(counts[e] >= 7 * 256 + 1 for e in heavy)
+    assert any(counts[e] < 8 * 256 for e in range(N) if e not in heavy)
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
