@@ -9,11 +9,12 @@
 // x*hi, x*mid, x*lo is exact in the fp32 accumulator of
 // v_mfma_f32_16x16x32_bf16: three matrix-core passes give fp32-accurate
 // scores at bf16 matrix-core rate instead of the fp32 vector rate.
-//   block: 128 tokens x 64 experts; wave w owns experts [16w, 16w+16) for all
-//   128 tokens; K in 64-element stages; x tile (128 B rows, bf16) and the raw
-//   fp32 weight tile (256 B rows) are filled by global_load_lds_dwordx4 into a
-//   4-stage LDS pipeline; the split happens in registers on the fragment read.
-//   XCD-aware order: the 12 expert tiles of one token tile run on one XCD.
+//   block: 128 tokens x 64 experts; compute wave w owns experts [16w, 16w+16)
+//   for all 128 tokens; K in 64-element stages; x tile (128 B rows, bf16) and
+//   the raw fp32 weight tile (256 B rows) are filled by global_load_lds_dwordx4
+//   from four loader waves into a 5-stage LDS ring; the split happens in
+//   registers on the fragment read.  XCD-aware order: the 12 expert tiles of
+//   one token tile run on one XCD.
 // fp32 activations (or H % 64 != 0): an LDS-tiled FMA kernel, 64 tokens x 64
 // experts per block, K step 16, a 4x4 patch per thread.  Any T, E, H.
 #include "moe_internal.h"
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void router_fma(const TX* __restrict__ x,
 }
 
 // ----------------------------------------------------- matrix-core path --
-constexpr int kRM = 128, kRN = 64, kRK = 64, kRStages = 4;
+constexpr int kRM = 128, kRN = 64, kRK = 64;
 constexpr int kAStage = kRM * kRK * 2;          // 16 KB of x
 constexpr int kBStage = kRN * kRK * 4;          // 16 KB of fp32 weights
 constexpr int kRStageBytes = kAStage + kBStage;
@@ -92,11 +93,22 @@ __device__ __forceinline__ void split3(const f32x4& v0, const f32x4& v1, bf16x8&
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void router_mfma(const bf16* __restrict__ x,
-                                                           const float* __restrict__ w, int T,
-                                                           int H, int E, int NTE,
-                                                           float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRStages * kRStageBytes];
+// 8 waves per block: waves 4-7 only issue the global->LDS loads of each
+// stage (x rows 8 per instruction, weight rows 4 per instruction), waves 0-3
+// only read fragments, split the weights and issue MFMAs -- a stalled load
+// issue then holds a loader, not a matrix core.  Every step issues the same
+// loads (past the end they read one fixed line into a stage no one reads
+// again), so every wait count is a constant.  The 12 expert tiles of one
+// token tile run on one XCD and re-read its x rows from L2; each starts its K
+// sweep at its own offset so that they do not all wait on the same miss.
+constexpr int kRThreads = 512;
+constexpr int kRS = 5;                          // ring stages (160 KB)
+
+__global__ __launch_bounds__(kRThreads, 1) void router_mfma(const bf16* __restrict__ x,
+                                                            const float* __restrict__ w, int T,
+                                                            int H, int E, int NTE,
+                                                            float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) char smem[kRS * kRStageBytes];
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int mt = (slot / NTE) * 8 + xcd;
@@ -104,49 +116,55 @@ __global__ __launch_bounds__(kThreads, 1) void router_mfma(const bf16* __restric
   const int m0 = mt * kRM, n0 = nt * kRN;
   if (m0 >= T) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KT = H / kRK;
+  const int k_start = (int)(((long long)nt * KT) / NTE) % KT;
 
-  // x: 16 instructions of 8 rows per stage (4 per wave)
-  const bf16* a_src[4];
+  if (wave >= 4) {
+    const int l = wave - 4;
+    const bf16* a_src[4];
+    const float* b_src[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (wave + 4 * q) * 8 + (lane >> 3);
-    a_src[q] = x + (size_t)min(m0 + r, T - 1) * H + swz8(r, lane & 7) * 8;
+    for (int q = 0; q < 4; ++q) {
+      const int ra = (l + 4 * q) * 8 + (lane >> 3);
+      a_src[q] = x + (size_t)min(m0 + ra, T - 1) * H + swz8(ra, lane & 7) * 8;
+      const int rb = (l + 4 * q) * 4 + (lane >> 4);
+      b_src[q] = w + (size_t)min(n0 + rb, E - 1) * H + swz16(rb, lane & 15) * 4;
+    }
+    auto issue = [&](int kt) {
+      char* sb = smem + (kt % kRS) * kRStageBytes;
+      int ks = kt + k_start;
+      ks = ks >= KT ? ks - KT : ks;
+      const int k0 = kt < KT ? ks * kRK : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+                                         (lds_void*)(sb + (l + 4 * q) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
+                                         (lds_void*)(sb + kAStage + (l + 4 * q) * 1024), 16, 0,
+                                         0);
+    };
+    for (int kt = 0; kt < kRS - 1; ++kt) issue(kt);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vmcnt<8 * (kRS - 2)>();   // step kt has landed (in-order completion)
+      lds_barrier();                 // publish it; every wave is done with step kt - 1
+      issue(kt + kRS - 1);           // into the stage step kt - 1 used
+    }
+    wait_vmcnt<0>();
+    lds_barrier();   // the LDS is free for the output tile
+    lds_barrier();   // the tile is written
+    return;
   }
-  // weights: 16 instructions of 4 rows (256 B each) per stage (4 per wave)
-  const float* b_src[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (wave + 4 * q) * 4 + (lane >> 4);
-    b_src[q] = w + (size_t)min(n0 + r, E - 1) * H + swz16(r, lane & 15) * 4;
-  }
-  auto issue = [&](int stage, int k0) {
-    char* sb = smem + stage * kRStageBytes;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
-                                       (lds_void*)(sb + (wave + 4 * q) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
-                                       (lds_void*)(sb + kAStage + (wave + 4 * q) * 1024), 16, 0,
-                                       0);
-  };
-  constexpr int kLoads = 8;
+
   f32x4 acc[kRM / 16];
 #pragma unroll
   for (int i = 0; i < kRM / 16; ++i) acc[i] = f32x4{0, 0, 0, 0};
-  const int KT = H / kRK;
-#pragma unroll
-  for (int s = 0; s < kRStages - 1; ++s)
-    if (s < KT) issue(s, s * kRK);
   const int rB = 16 * wave + (lane & 15);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + kRStages - 1 <= KT) wait_vmcnt<kLoads * (kRStages - 2)>();
-    else wait_vmcnt<0>();
     lds_barrier();
-    if (kt + kRStages - 1 < KT) issue((kt + kRStages - 1) % kRStages, (kt + kRStages - 1) * kRK);
-    const char* As = smem + (kt % kRStages) * kRStageBytes;
+    const char* As = smem + (kt % kRS) * kRStageBytes;
     const char* Bs = As + kAStage;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -167,15 +185,35 @@ __global__ __launch_bounds__(kThreads, 1) void router_mfma(const bf16* __restric
       }
     }
   }
-  const int col = n0 + 16 * wave + (lane & 15);
-  if (col >= E) return;
+  // Output through LDS: [128 tokens][64 experts] fp32 (row pitch 272 B), then
+  // 16 bytes per lane to logits -- whole 256 B row pieces per 16 lanes
+  // instead of one 4-byte value per lane per store instruction.
+  constexpr int kPitch = kRN * 4 + 16;
+  static_assert(kRM * kPitch <= kRS * kRStageBytes, "output tile fits the ring");
+  lds_barrier();   // loads landed, fragments read: the LDS is free
 #pragma unroll
   for (int rb = 0; rb < kRM / 16; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = m0 + rb * 16 + 4 * (lane >> 4) + i;
-      if (t < T) logits[(size_t)t * E + col] = acc[rb][i];
+      const int r = rb * 16 + 4 * (lane >> 4) + i;
+      *(float*)(smem + r * kPitch + (16 * wave + (lane & 15)) * 4) = acc[rb][i];
     }
+  lds_barrier();   // the four compute waves' values are in the tile
+  // whole 16-byte pieces: in range and 16-byte aligned
+  const bool full = n0 + kRN <= E && (E & 3) == 0 && ((uintptr_t)logits & 15) == 0;
+  for (int j = threadIdx.x; j < kRM * (kRN / 4); j += 256) {
+    const int r = j / (kRN / 4), cq = j % (kRN / 4);
+    if (m0 + r >= T) continue;
+    const f32x4 v = *(const f32x4*)(smem + r * kPitch + cq * 16);
+    float* dst = logits + (size_t)(m0 + r) * E + n0 + 4 * cq;
+    if (full) {
+      *(f32x4*)dst = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n0 + 4 * cq + u < E) dst[u] = v[u];
+    }
+  }
 }
 
 }  // namespace
@@ -186,8 +224,8 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
     const int nte = (E + kRN - 1) / kRN;
     const unsigned groups = ceil_div(ceil_div(T, kRM), 8);
     MOE_LAUNCH("router_logits", s,
-               router_mfma<<<groups * 8 * nte, kThreads, 0, s>>>((const bf16*)x, w, T, H, E, nte,
-                                                                 logits));
+               router_mfma<<<groups * 8 * nte, kRThreads, 0, s>>>((const bf16*)x, w, T, H, E,
+                                                                  nte, logits));
     return hipGetLastError();
   }
   dim3 grid(ceil_div(E, kTN), ceil_div(T, kTM));
