@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256) void perm_gather(const i32x4* __restrict__ x, 
 #pragma unroll
     for (int j = 0; j < VEC_PER_THREAD; ++j) {
       int c = threadIdx.x + 256 * j;
-      if (c < row_vecs) dst[c] = v[j];
+      // non-temporal: streamed out now, not written back during the GEMM
+      if (c < row_vecs) __builtin_nontemporal_store(v[j], dst + c);
     }
   }
 }
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void perm_gather_long(const i32x4* __restrict_
     const int row = slot_row[(size_t)t * K + k];
     if (row < 0) continue;
     i32x4* dst = x_perm + (size_t)row * row_vecs;
-    for (int c = threadIdx.x; c < row_vecs; c += 256) dst[c] = src[c];
+    for (int c = threadIdx.x; c < row_vecs; c += 256) __builtin_nontemporal_store(src[c], dst + c);
   }
 }
 
