@@ -69,6 +69,8 @@ def _load():
             D = ctypes.c_double
             lib.oracle_bias_update.argtypes = [P, I, I, D, D, D, D, P, P, P]
             lib.oracle_bias_update.restype = None
+            lib.oracle_router_similarity.argtypes = [P, I, I, P]
+            lib.oracle_router_similarity.restype = D
             _lib = lib
     return _lib
 
@@ -252,6 +254,18 @@ def bias_update(counts: np.ndarray, T: int, n_ffn: int, target: float, kp: float
     lib.oracle_bias_update(_p(counts), int(T), int(n_ffn), float(target), float(kp), float(ki),
                            float(kd), _p(bias), _p(integral), _p(prev))
     return bias, integral, prev
+
+
+def router_similarity(w: np.ndarray):
+    """Pairwise cosine similarity of the router's per-expert weight rows and
+    its mean over the pairs i != j (see ``oracle_router_similarity``).
+    w: [E, H] fp32.  Returns (sim [E, E] fp64, mean)."""
+    lib = _load()
+    w = _c(w, np.float32)
+    E, H = w.shape
+    sim = np.empty((E, E), np.float64)
+    mean = lib.oracle_router_similarity(_p(w), int(E), int(H), _p(sim))
+    return sim, float(mean)
 
 
 # ------------------------------------------------------------ whole layer ----

@@ -255,3 +255,36 @@ void oracle_bias_update(const int32_t *counts, int T, int n_ffn, double target, 
         prev[i] = err;
     }
 }
+
+/* ---- router weight similarity --------------------------------------------
+ * The report watches router stability through the pairwise cosine similarity
+ * of the experts' router weight vectors (high similarity marks a router
+ * collapsed by the load-balance term) -- Technical Report notes, Key claims
+ * and Method [§3.1.3 Router Stability].  The vectors are the rows of w_router.
+ *   dot[i][j] = sum_h w[i][h] * w[j][h]          (fp64, h ascending)
+ *   sim[i][j] = dot[i][j] / (sqrt(dot[i][i]) * sqrt(dot[j][j]))
+ * A row of zero norm has similarity 0 with every row, itself included.
+ * Returns the mean of sim over the E*(E-1) ordered pairs i != j (0 if E = 1). */
+double oracle_router_similarity(const float *w, int E, int H, double *sim)
+{
+    double *norm = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    for (int i = 0; i < E; ++i) {
+        double acc = 0.0;
+        for (int h = 0; h < H; ++h)
+            acc += (double)w[(size_t)i * H + h] * (double)w[(size_t)i * H + h];
+        norm[i] = sqrt(acc);
+    }
+    double total = 0.0;
+    for (int i = 0; i < E; ++i) {
+        for (int j = 0; j < E; ++j) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += (double)w[(size_t)i * H + h] * (double)w[(size_t)j * H + h];
+            double c = (norm[i] > 0.0 && norm[j] > 0.0) ? acc / (norm[i] * norm[j]) : 0.0;
+            sim[(size_t)i * E + j] = c;
+            if (i != j) total += c;
+        }
+    }
+    free(norm);
+    return E > 1 ? total / ((double)E * (double)(E - 1)) : 0.0;
+}

@@ -453,3 +453,74 @@ def test_bias_update_derivative_opposes_a_rising_load():
     moved = np.array([24, 8, 16, 16, 32], np.int32)
     nb, _, _ = oracle.bias_update(moved, T, N, 2.0, 0.0, 0.0, 0.8, b, i, p)
     assert nb[0] < 0 < nb[1] and nb[2] == nb[3] == 0
+
+
+# ------------------------------------------------ router weight similarity --
+# Pairwise cosine similarity of the experts' router weight rows, the router
+# stability diagnostic (Technical Report notes, Key claims and Method
+# [§3.1.3 Router Stability]).
+
+def test_similarity_matches_scipy_cosine_distance():
+    from scipy.spatial.distance import cdist
+    w = _rng(60).standard_normal((23, 41)).astype(np.float32)
+    sim, mean = oracle.router_similarity(w)
+    ref = 1.0 - cdist(w.astype(np.float64), w.astype(np.float64), "cosine")
+    np.testing.assert_allclose(sim, ref, rtol=0, atol=1e-12)
+    off = ref[~np.eye(23, dtype=bool)]
+    assert abs(mean - off.mean()) < 1e-12
+
+
+def test_similarity_of_a_regular_simplex():
+    # E unit vectors centred on their mean: every pair has cosine -1/(E-1),
+    # rotated into a wider space so rows are not axis-aligned.
+    E, H = 9, 30
+    v = np.eye(E) - 1.0 / E
+    q, _ = np.linalg.qr(_rng(61).standard_normal((H, H)))
+    w = (v @ q[:E, :]).astype(np.float32)
+    sim, mean = oracle.router_similarity(w)
+    off = sim[~np.eye(E, dtype=bool)]
+    np.testing.assert_allclose(off, -1.0 / (E - 1), atol=1e-6)
+    np.testing.assert_allclose(np.diag(sim), 1.0, atol=1e-12)
+    assert abs(mean + 1.0 / (E - 1)) < 1e-6
+
+
+def test_similarity_orthogonal_and_identical_rows():
+    q, _ = np.linalg.qr(_rng(62).standard_normal((16, 16)))
+    sim, mean = oracle.router_similarity(q[:10].astype(np.float32))
+    np.testing.assert_allclose(sim, np.eye(10), atol=1e-6)
+    assert abs(mean) < 1e-6
+    row = _rng(63).standard_normal(50).astype(np.float32)
+    sim, mean = oracle.router_similarity(np.stack([row, 3 * row, 0.5 * row]))
+    np.testing.assert_allclose(sim, 1.0, atol=1e-12)
+    assert abs(mean - 1.0) < 1e-12
+
+
+def test_similarity_scale_sign_and_zero_rows():
+    w = _rng(64).standard_normal((12, 33)).astype(np.float32)
+    sim, _ = oracle.router_similarity(w)
+    w2 = w.copy()
+    w2[3] *= 4.0    # exact in fp32
+    w2[5] *= -1.0
+    w2[7] = 0.0
+    sim2, mean2 = oracle.router_similarity(w2)
+    sign = np.ones(12)
+    sign[5] = -1.0
+    expect = sim * sign[:, None] * sign[None, :]
+    expect[7, :] = 0.0
+    expect[:, 7] = 0.0
+    np.testing.assert_allclose(sim2, expect, atol=1e-12)
+    assert abs(mean2 - expect[~np.eye(12, dtype=bool)].mean()) < 1e-12
+    assert sim2[7, 7] == 0.0
+
+
+def test_similarity_separates_collapsed_from_random_routers():
+    r = _rng(65)
+    E, H = 64, 256
+    _, m_rand = oracle.router_similarity(r.standard_normal((E, H)).astype(np.float32))
+    assert abs(m_rand) < 4.0 / np.sqrt(H) / np.sqrt(E)
+    common = r.standard_normal(H)
+    w = (common + 0.1 * r.standard_normal((E, H))).astype(np.float32)
+    _, m_col = oracle.router_similarity(w)
+    assert m_col > 0.95
+    sim, mean = oracle.router_similarity(w[:1])
+    assert sim.shape == (1, 1) and abs(sim[0, 0] - 1.0) < 1e-12 and mean == 0.0
