@@ -36,6 +36,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_traffic.json")
 FFN_SOURCE = os.path.join(ROOT, "sparse_moe_layer_02_amd", "csrc", "ffn.hip")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM MFMA util and HBM GB/s vs peak"
 
 
@@ -87,6 +88,35 @@ def measured_traffic(workload_name):
     if rec.get("source_sha256") != src or rec.get("workload") != workload_name:
         return None
     return int(rec["bytes_per_launch"])
+
+
+def router_similarity(w_router, reps=20):
+    """The router-stability diagnostic on the workload's router weights, timed
+    apart from the forward pass (it is not part of a step): per-kernel mean
+    microseconds and the Gram kernel's rate against the fp32 matrix peak.
+    Algorithmic FLOPs: the E(E+1)/2 distinct dot products of length H."""
+    E, H = w_router.shape
+    dev = w_router.device
+    sim = torch.empty((E, E), dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_router_similarity_workspace_bytes(E, H), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(3):
+        moe.moe_router_similarity(w_router, sim, mean, ws)
+    torch.cuda.synchronize(dev)
+    moe.moe_profile_enable(True)
+    for _ in range(reps):
+        moe.moe_router_similarity(w_router, sim, mean, ws)
+    torch.cuda.synchronize(dev)
+    moe.moe_profile_enable(False)
+    kern = moe.moe_profile_summary()
+    us = {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()}
+    flops = float(E) * (E + 1) * H
+    gram_s = kern["sim_gram"][1] / kern["sim_gram"][0] * 1e-3
+    return dict(rows=E, hidden=H, mean_cosine=float(mean.item()), kernels_us=us,
+                total_us=round(sum(us.values()), 1),
+                gram_tflops=round(flops / gram_s / 1e12, 2),
+                gram_mfma_f32_frac=round(flops / gram_s / 1e12 / MFMA_F32_PEAK_TFLOPS, 4))
 
 
 def cpu_baseline(cfg, inp, n_tokens):
@@ -222,6 +252,7 @@ def main():
                                          / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()},
     }
+    result["router_similarity"] = router_similarity(inp["w_router"])
     if args.cpu_tokens > 0:
         print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr,
               flush=True)

@@ -158,6 +158,26 @@ moe_status moe_bias_update(const int32_t *counts, int T, int n_ffn, float target
                            float ki, float kd, float *bias, float *integral, float *prev_err,
                            void *stream);
 
+/* Router weight similarity (Technical Report notes, Key claims and Method
+ * [§3.1.3 Router Stability]: the pairwise cosine similarity of the experts'
+ * router weight vectors is tracked as a router-stability diagnostic; high
+ * values mark a router collapsed by the load-balance term).
+ *   sim[i][j] = <w_i, w_j> / (|w_i| * |w_j|)   for rows w_i of w_router,
+ *               0 when either row has zero norm (the diagonal too);
+ *   *mean     = average of sim[i][j] over the E*(E-1) pairs i != j
+ *               (0 when E = 1).
+ * w_router: [E][H] fp32, 16-byte aligned, H % 4 == 0 (pass the first n_ffn
+ * rows to restrict the diagnostic to the FFN experts).  sim: [E][E] fp32,
+ * exactly symmetric.  mean: one fp32 in device memory.  fp32 products and
+ * accumulation on the matrix cores, the row sums and the mean in fp64.
+ * ws: at least moe_router_similarity_workspace_bytes(E, H) bytes, 256-byte
+ * aligned (partial Gram tiles, norms and row sums; contents need not be
+ * initialised).
+ * MOE_ERR_SHAPE: E or H < 1, H % 4 != 0, or E*E >= 2^31. */
+size_t moe_router_similarity_workspace_bytes(int E, int H);
+moe_status moe_router_similarity(const float *w_router, int E, int H, float *sim, float *mean,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* Diagnostics (not part of the layer): opt-in per-kernel timing.  While
  * enabled, each kernel the calls above enqueue is bracketed by two HIP events
  * recorded on its stream.  moe_profile_enable(1) starts a new session (the

@@ -39,6 +39,8 @@ _SIGS = {
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
     "moe_bias_update": ([_P, _I, _I, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                          ctypes.c_float, _P, _P, _P, _P], _I),
+    "moe_router_similarity_workspace_bytes": ([_I, _I], ctypes.c_size_t),
+    "moe_router_similarity": ([_P, _I, _I, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_profile_enable": ([_I], _I),
     "moe_profile_summary": ([ctypes.c_char_p, ctypes.c_size_t], _I),
@@ -197,6 +199,25 @@ def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_e
     _check("moe_bias_update", lib().moe_bias_update(
         _ptr(counts), int(T), int(n_ffn), float(target), float(kp), float(ki), float(kd),
         _ptr(bias), _ptr(integral), _ptr(prev_err), _stream(bias)))
+
+
+def moe_router_similarity_workspace_bytes(E, H):
+    return int(lib().moe_router_similarity_workspace_bytes(E, H))
+
+
+def moe_router_similarity(w_router, sim, mean, ws):
+    """Pairwise cosine similarity of the router's per-expert weight rows into
+    sim [E, E] and its off-diagonal mean into mean [1] (fp32 tensors)."""
+    _dev(w_router, sim, mean, ws)
+    _want(w_router, torch.float32, "w_router")
+    _want(sim, torch.float32, "sim")
+    _want(mean, torch.float32, "mean")
+    E, H = w_router.shape
+    assert sim.shape == (E, E) and mean.numel() >= 1
+    assert w_router.is_contiguous() and sim.is_contiguous()
+    _check("moe_router_similarity", lib().moe_router_similarity(
+        _ptr(w_router), E, H, _ptr(sim), _ptr(mean), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(w_router)))
 
 
 # ------------------------------------------------------------ diagnostics --

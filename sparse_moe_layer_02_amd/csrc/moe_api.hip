@@ -144,4 +144,19 @@ moe_status moe_bias_update(const int32_t* counts, int T, int n_ffn, float target
                                      prev_err, (hipStream_t)stream));
 }
 
+size_t moe_router_similarity_workspace_bytes(int E, int H) {
+  if (E < 1 || H < 1 || H % 4 || !fits_i32((long long)E * E)) return 0;
+  return similarity_ws_bytes(E, H);
+}
+
+moe_status moe_router_similarity(const float* w_router, int E, int H, float* sim, float* mean,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!w_router || !sim || !mean || !ws) return MOE_ERR_NULL;
+  if (E < 1 || H < 1 || H % 4 || !fits_i32((long long)E * E)) return MOE_ERR_SHAPE;
+  if (!aligned(w_router, 16) || !aligned(sim, 4) || !aligned(mean, 4) || !aligned(ws, 256))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < similarity_ws_bytes(E, H)) return MOE_ERR_WORKSPACE;
+  return launched(launch_router_similarity(w_router, E, H, sim, mean, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -81,5 +81,8 @@ hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row
 hipError_t launch_bias_update(const int32_t* counts, int T, int n_ffn, float target, float kp,
                               float ki, float kd, float* bias, float* integral, float* prev,
                               hipStream_t s);
+size_t similarity_ws_bytes(int E, int H);
+hipError_t launch_router_similarity(const float* w, int E, int H, float* sim, float* mean,
+                                    void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -143,3 +143,27 @@ def test_bias_update_validation():
     assert f(*a) == SHAPE
     a = list(args); a[8] = P(0x10002)
     assert f(*a) == ALIGN
+
+
+def test_router_similarity_validation():
+    lib = moe.lib()
+    f = lib.moe_router_similarity
+    need = lib.moe_router_similarity_workspace_bytes(768, 6144)
+    # partial 64 x 64 Gram tiles of 78 triangle tiles, at least one K split
+    assert need >= 78 * 64 * 64 * 4
+    assert lib.moe_router_similarity_workspace_bytes(768, 6) == 0        # H % 4
+    assert lib.moe_router_similarity_workspace_bytes(0, 64) == 0
+    assert lib.moe_router_similarity_workspace_bytes(50000, 64) == 0     # E * E >= 2^31
+    args = [FAKE, 768, 6144, FAKE, FAKE, FAKE, need, None]
+    a = list(args); a[4] = None
+    assert f(*a) == NULL
+    a = list(args); a[2] = 6142
+    assert f(*a) == SHAPE
+    a = list(args); a[1] = 0
+    assert f(*a) == SHAPE
+    a = list(args); a[0] = P(0x10004)                  # w_router needs 16 bytes
+    assert f(*a) == ALIGN
+    a = list(args); a[5] = P(0x10080)                  # workspace needs 256 bytes
+    assert f(*a) == ALIGN
+    a = list(args); a[6] = need - 1
+    assert f(*a) == WS
