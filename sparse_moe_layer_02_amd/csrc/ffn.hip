@@ -322,9 +322,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   // same activation rows.  Swept in lockstep, every one of them would wait on
   // the same L2 miss at every step; starting each tile's K sweep at its own
   // offset (and wrapping around) spreads the first touches out, so the other
-  // tiles hit L2.
+  // tiles hit L2.  Full 256-row tiles (heavy experts, whose activation rows
+  // fill most of an XCD's L2) use four offsets only: four streams through
+  // the m-tile keep more of it resident (measured 7-14 % faster on experts
+  // of 2048-16384 rows than one offset per column tile).
   const int KT = KD / kBK;
-  const int k_start = (int)(((long long)nt * KT) / NT) % KT;
+  const int k_start = rows == kBmBf16 ? ((nt & 3) * KT) / 4 : (int)(((long long)nt * KT) / NT) % KT;
 
   const int groups = (rows + 31) >> 5;
   if (wave >= 4) {   // loader waves
