@@ -28,9 +28,9 @@
 //     128-byte lines), not one 2-byte value per lane per instruction;
 //   - block -> tile order is XCD-aware: consecutive blocks land on the 8 XCDs
 //     in turn, so all column tiles of one m-tile run on one XCD and re-read
-//     the m-tile's activation rows from that XCD's L2; each column tile starts
-//     its K sweep at its own offset so that those re-reads are L2 hits rather
-//     than 32 simultaneous waits on one miss.
+//     the m-tile's activation rows from that XCD's L2; the column tiles start
+//     their K sweeps at a few different offsets, so that those re-reads are L2
+//     hits rather than 32 simultaneous waits on one miss.
 #include "moe_internal.h"
 
 namespace moe {
@@ -319,15 +319,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   const TileSrc src{A + (size_t)row0 * KD, rows, W + (size_t)e * wrows * KD, nt, I, GATEUP,
                     GATEUP ? KD : kBK, GATEUP ? kBK : rows * kBK};
   // The column tiles of one m-tile run side by side on one XCD and read the
-  // same activation rows.  Swept in lockstep, every one of them would wait on
-  // the same L2 miss at every step; starting each tile's K sweep at its own
-  // offset (and wrapping around) spreads the first touches out, so the other
-  // tiles hit L2.  Full 256-row tiles (heavy experts, whose activation rows
-  // fill most of an XCD's L2) use four offsets only: four streams through
-  // the m-tile keep more of it resident (measured 7-14 % faster on experts
-  // of 2048-16384 rows than one offset per column tile).
+  // same activation rows.  Swept in lockstep, every one of them waits on the
+  // same L2 miss at every step; spread over the whole K range, the m-tile's
+  // rows are all live at once and crowd L2.  Tiles start their K sweep (and
+  // wrap around) at one of a few offsets, by column tile: four for full
+  // 256-row tiles (3 MB of activation rows), two for the partial tiles of
+  // gate/up (~1.5 MB at the prefill shape), and one for the partial tiles of
+  // down, whose m-tile is a few hundred KB.  Measured against one offset per
+  // column tile: prefill gate/up 5.38 -> 5.23 ms, down 2.90 -> 2.88 ms, and
+  // 7-14 % on experts of 2048-16384 rows.  Tiles of one 32-row group (decode)
+  // keep one offset per column tile, which measured 0.4 % faster there.
   const int KT = KD / kBK;
-  const int k_start = rows == kBmBf16 ? ((nt & 3) * KT) / 4 : (int)(((long long)nt * KT) / NT) % KT;
+  const int n_start = rows == kBmBf16 ? 4 : rows <= 32 ? NT : (GATEUP ? 2 : 1);
+  const int k_start = ((nt % n_start) * KT) / n_start;
 
   const int groups = (rows + 31) >> 5;
   if (wave >= 4) {   // loader waves
