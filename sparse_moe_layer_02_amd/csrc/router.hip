@@ -99,8 +99,9 @@ __device__ __forceinline__ void split3(const f32x4& v0, const f32x4& v1, bf16x8&
 // issue then holds a loader, not a matrix core.  Every step issues the same
 // loads (past the end they read one fixed line into a stage no one reads
 // again), so every wait count is a constant.  The 12 expert tiles of one
-// token tile run on one XCD and re-read its x rows from L2; each starts its K
-// sweep at its own offset so that they do not all wait on the same miss.
+// token tile run on one XCD and re-read its x rows from L2; they start their
+// K sweeps at two offsets (by tile parity) so that they do not all wait on
+// the same miss.  Two offsets measured 2-8 % faster than one per tile.
 constexpr int kRThreads = 512;
 constexpr int kRS = 5;                          // ring stages (160 KB)
 
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kRThreads, 1) void router_mfma(const bf16* __restri
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int KT = H / kRK;
-  const int k_start = (int)(((long long)nt * KT) / NTE) % KT;
+  const int k_start = ((nt & 1) * KT) / 2;   // two offsets (see above)
 
   if (wave >= 4) {
     const int l = wave - 4;
