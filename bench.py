@@ -37,6 +37,17 @@ FFN_SOURCE = os.path.join(ROOT, "sparse_moe_layer_02_amd", "csrc", "ffn.hip")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
+# The calls of one forward pass and the kernels each one launches.
+CALLS = {
+    "moe_router_logits": ("router_logits",),
+    "moe_route": ("route_clear", "route_topk"),
+    "moe_permute": ("permute_hist", "permute_scan_blocks", "permute_scan_experts",
+                    "permute_scatter", "permute_gather"),
+    "moe_expert_ffn": ("ffn_tiles", "ffn_gateup_bf16", "ffn_gateup_dense_bf16", "ffn_down_bf16",
+                       "ffn_down_dense_bf16", "ffn_gateup_f32", "ffn_down_f32"),
+    "moe_zero_experts": ("zero_experts",),
+    "moe_combine": ("combine",),
+}
 METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM MFMA util and HBM GB/s vs peak"
 
 
@@ -52,6 +63,10 @@ def parse():
     p.add_argument("--bias-controller", type=float, default=0.0, metavar="TARGET",
                    help="also run one bias-controller update per step (moe_bias_update, "
                         "FFN experts per token held at TARGET; gains 1.0/0.05/0.2)")
+    p.add_argument("--flush-mib", type=int, default=0,
+                   help="write a scratch buffer of this many MiB before every timed step "
+                        "(outside the step's events) so that small layers do not run from the "
+                        "256 MB Infinity Cache; ms_per_step is then the mean of per-step events")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -72,6 +87,52 @@ def algorithmic(cfg, counts, S):
     down_flops = 2.0 * S * I * H
     return dict(active=active, gateup_bytes=gateup_bytes, down_bytes=down_bytes,
                 gateup_flops=gateup_flops, down_flops=down_flops)
+
+
+def call_floors(cfg, counts, S, kern):
+    """Per call of the forward pass: measured microseconds, algorithmic bytes
+    (inputs read once, outputs written once, weights of active experts read
+    once) and FLOPs, the floor max(bytes / HBM peak, FLOPs / matrix peak),
+    and the call's fraction of its floor.  The router's FLOPs are counted as
+    the three bf16 matrix passes it runs on bf16 layers (an fp32-exact
+    product), against the bf16 peak; on fp32 layers as one pass against the
+    fp32 peak."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, H, E, N, I, K = cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K
+    alg = algorithmic(cfg, counts, S)
+    mm_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    router_flops = 2.0 * T * E * H * (3 if cfg.dtype == "bf16" else 1)
+    work = {
+        "moe_router_logits": (T * H * es + E * H * 4 + T * E * 4, router_flops),
+        "moe_route": (T * E * 4 + E * 4 + T * K * 8 + E * 8, 0.0),
+        "moe_permute": (T * K * 4 * 2 + (N + 1) * 4 + S * 4 + T * K * 4 + T * H * es + S * H * es,
+                        0.0),
+        "moe_expert_ffn": (alg["gateup_bytes"] + alg["down_bytes"],
+                           alg["gateup_flops"] + alg["down_flops"]),
+        "moe_zero_experts": (T * H * es + T * H * 4 + T * K * 8, 0.0),
+        "moe_combine": (S * H * es + T * H * 4 + T * H * es + T * K * 8, 0.0),
+    }
+    out = {}
+    for call, names in CALLS.items():
+        us = sum(kern[n][1] / kern[n][0] * 1e3 for n in names if n in kern)
+        nbytes, flops = work[call]
+        floor_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (mm_peak * 1e6))
+        out[call] = dict(us=round(us, 1), bytes=int(nbytes), gflop=round(flops / 1e9, 2),
+                         floor_us=round(floor_us, 1),
+                         frac_of_floor=round(floor_us / us, 3) if us > 0 else None)
+    return out
+
+
+def routing_stats(cfg, counts, S):
+    """Realised routing of the timed batch: FFN share of the T*K picks and
+    rows per active FFN expert."""
+    rows = counts[:cfg.N]
+    act = rows[rows > 0]
+    return dict(ffn_share=round(S / (cfg.T * cfg.K), 4), identity_picks=int(cfg.T * cfg.K - S),
+                active_ffn_experts=int(act.size),
+                rows_per_active_expert={"min": int(act.min()) if act.size else 0,
+                                        "median": float(np.median(act)) if act.size else 0.0,
+                                        "max": int(act.max()) if act.size else 0})
 
 
 def measured_traffic(workload_name):
@@ -196,14 +257,26 @@ def main():
 
     moe.moe_profile_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.flush_mib > 0:
+        scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if args.flush_mib > 0:
+            scratch.fill_(i & 0xFF)
+            evs[i][0].record(stream)
         step()
+        if args.flush_mib > 0:
+            evs[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize(dev)
     moe.moe_profile_enable(False)
-    ms = start.elapsed_time(end) / args.steps
+    if args.flush_mib > 0:
+        ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    else:
+        ms = start.elapsed_time(end) / args.steps
     kern = moe.moe_profile_summary()
 
     counts = buf["counts"].cpu().numpy()
@@ -251,7 +324,11 @@ def main():
                       "mfma_frac": round(alg["down_flops"] / (d_ms * 1e-3) / 1e12
                                          / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()},
+        "calls": call_floors(cfg, counts, S, kern),
+        "routing": routing_stats(cfg, counts, S),
     }
+    if args.flush_mib > 0:
+        result["cache_flush_mib_between_steps"] = args.flush_mib
     result["router_similarity"] = router_similarity(inp["w_router"])
     if args.cpu_tokens > 0:
         print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr,
