@@ -15,6 +15,8 @@
 //   from four loader waves into a 5-stage LDS ring; the split happens in
 //   registers on the fragment read.  XCD-aware order: the 12 expert tiles of
 //   one token tile run on one XCD.
+// bf16 activations with T <= 64 and H % 256 == 0 (decode): 16 experts per
+// block, H split over the block's 8 waves (router_small below).
 // fp32 activations (or H % 64 != 0): an LDS-tiled FMA kernel, 64 tokens x 64
 // experts per block, K step 16, a 4x4 patch per thread.  Any T, E, H.
 #include "moe_internal.h"
@@ -217,10 +219,89 @@ __global__ __launch_bounds__(kRThreads, 1) void router_mfma(const bf16* __restri
   }
 }
 
+// ------------------------------------------------- few tokens (decode) --
+// With T <= 64 the 128 x 64 tiles above leave a dozen blocks for the whole
+// chip, each streaming 64 experts' weights over all of H.  Here a block takes
+// 16 experts and all T tokens, and its 8 waves split H into 8 ranges.  Each
+// wave loads its fragments straight from global memory (nothing is reused
+// inside the block), splits the weights into the three bf16 planes and
+// accumulates; the 8 partial tiles are then added through LDS in wave order,
+// a fixed order, so the result is bitwise reproducible.
+constexpr int kSmallT = 64;       // tokens per block: all of them
+constexpr int kSmallN = 16;       // experts per block
+constexpr int kSmallWaves = 8;    // K ranges
+constexpr int kSmallU = 4;        // 32-element k slices in flight per wave
+
+__global__ __launch_bounds__(kSmallWaves * kWave) void router_small(const bf16* __restrict__ x,
+                                                                    const float* __restrict__ w,
+                                                                    int T, int H, int E,
+                                                                    float* __restrict__ logits) {
+  __shared__ float part[kSmallWaves][kSmallT][kSmallN];
+  const int n0 = blockIdx.x * kSmallN;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int kr = H / kSmallWaves;   // a multiple of 32 (H % 256 == 0)
+  const int kbeg = wave * kr;
+  // v_mfma_f32_16x16x32_bf16 fragments: lane l holds row / column l & 15 and
+  // k elements 8 (l >> 4) .. + 8 of a 32-element slice.  Rows past T and
+  // experts past E are clamped and their results dropped.
+  const float* wrow = w + (size_t)min(n0 + (lane & 15), E - 1) * H + kbeg + 8 * (lane >> 4);
+  const bf16* xrow[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    xrow[rb] = x + (size_t)min(16 * rb + (lane & 15), T - 1) * H + kbeg + 8 * (lane >> 4);
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+  for (int k = 0; k < kr; k += 32 * kSmallU) {
+    f32x4 w0[kSmallU], w1[kSmallU];
+    bf16x8 xa[kSmallU][4];
+#pragma unroll
+    for (int u = 0; u < kSmallU; ++u) {
+      const int kk = min(k + 32 * u, kr - 32);   // past the range: a valid slice, not used
+      w0[u] = *(const f32x4*)(wrow + kk);
+      w1[u] = *(const f32x4*)(wrow + kk + 4);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) xa[u][rb] = *(const bf16x8*)(xrow[rb] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallU; ++u) {
+      if (k + 32 * u >= kr) break;   // wave-uniform
+      bf16x8 bh, bm, bl;
+      split3(w0[u], w1[u], bh, bm, bl);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bl, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bm, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bh, acc[rb], 0, 0, 0);
+      }
+    }
+  }
+  // acc[rb] element i: token 16 rb + 4 (l >> 4) + i, expert n0 + (l & 15)
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][16 * rb + 4 * (lane >> 4) + i][lane & 15] = acc[rb][i];
+  __syncthreads();
+  for (int j = threadIdx.x; j < kSmallT * kSmallN; j += kSmallWaves * kWave) {
+    const int t = j / kSmallN, c = j % kSmallN;
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kSmallWaves; ++v) sum += part[v][t][c];
+    if (t < T && n0 + c < E) logits[(size_t)t * E + n0 + c] = sum;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int H, int E,
                                 float* logits, hipStream_t s) {
+  if (dtype == MOE_BF16 && T <= kSmallT && H % (kSmallWaves * 32) == 0) {
+    MOE_LAUNCH("router_logits", s,
+               router_small<<<ceil_div(E, kSmallN), kSmallWaves * kWave, 0, s>>>(
+                   (const bf16*)x, w, T, H, E, logits));
+    return hipGetLastError();
+  }
   if (dtype == MOE_BF16 && H % kRK == 0) {
     const int nte = (E + kRN - 1) / kRN;
     const unsigned groups = ceil_div(ceil_div(T, kRM), 8);
