@@ -197,3 +197,29 @@ def test_heavy_experts_many_m_tiles(T, H, I, heavy, boost):
     assert any(counts[e] < 8 * 256 for e in range(N) if e not in heavy)
     stage_checks(cfg, inp, buf)
     _e2e(cfg, inp, buf)
+
+
+def test_two_stream_forward_matches_serial():
+    # For large batches forward() runs the identity experts on a second
+    # stream; combine must wait for them.  Two different batches alternate and
+    # y_acc is poisoned before every call, so a combine that read y_acc early
+    # would see NaN or the other batch's values.
+    cfg = workload.CONFIGS["mid_bf16"].replace(T=2048)
+    assert cfg.T >= moe.OVERLAP_MIN_TOKENS
+    dev = device()
+    inps = [workload.make_inputs(cfg.replace(seed=s), dev) for s in (0, 1)]
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+
+    def run(fn, inp):
+        buf["y_acc"].fill_(float("nan"))
+        y = fn(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.scale,
+               buf)
+        return y.clone()
+
+    ref = [run(moe.forward_serial, inp) for inp in inps]
+    for _ in range(3):
+        for i, inp in enumerate(inps):
+            got = run(moe.forward, inp)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref[i])
+    assert not torch.equal(ref[0], ref[1])
