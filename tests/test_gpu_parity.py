@@ -82,6 +82,20 @@ def test_k_equals_e_picks_every_expert():
     _e2e(cfg, inp, buf)
 
 
+@pytest.mark.parametrize("T", [40, 300])
+def test_largest_expert_pool(T):
+    # E = 1024, the most the routing kernel takes: 16 keys per lane, a
+    # 1024-bin pick histogram, 16 expert tiles in the router (T = 300) or 64
+    # 16-expert blocks of the few-token router (T = 40).
+    cfg = workload.MoEConfig("e1024", T=T, H=256, N=768, Z=256, I=128, K=12, dtype="bf16",
+                             sigma_w=0.05, bias_lo=-0.1, bias_hi=0.1, scale=1.0)
+    inp, buf = _run(cfg)
+    stage_checks(cfg, inp, buf)
+    counts = host(buf["counts"])
+    assert counts.sum() == cfg.T * cfg.K and counts.max() <= cfg.T
+    _e2e(cfg, inp, buf)
+
+
 def test_all_zero_expert_routing_returns_scaled_x():
     cfg = workload.MoEConfig("all_zero", T=130, H=256, N=6, Z=4, I=128, K=3, dtype="bf16",
                              sigma_w=0.05, bias_lo=0.0, bias_hi=0.0, scale=1.0)
