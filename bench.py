@@ -67,6 +67,9 @@ def parse():
                    help="write a scratch buffer of this many MiB before every timed step "
                         "(outside the step's events) so that small layers do not run from the "
                         "256 MB Infinity Cache; ms_per_step is then the mean of per-step events")
+    p.add_argument("--grouped-copy", action="store_true",
+                   help="dispatch copies the grouped x rows (moe_permute into x_perm, then "
+                        "moe_expert_ffn) instead of the expert GEMM gathering them from x")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -81,7 +84,7 @@ def algorithmic(cfg, counts, S):
     H, I = cfg.H, cfg.I
     w13 = active * 2 * I * H * es
     w2 = active * H * I * es
-    gateup_bytes = w13 + S * H * es + S * I * es        # weights + x_perm rows + hh rows
+    gateup_bytes = w13 + S * H * es + S * I * es        # weights + grouped x rows + hh rows
     down_bytes = w2 + S * I * es + S * H * es           # weights + hh rows + y_perm rows
     gateup_flops = 2.0 * S * H * 2 * I
     down_flops = 2.0 * S * I * H
@@ -89,14 +92,16 @@ def algorithmic(cfg, counts, S):
                 gateup_flops=gateup_flops, down_flops=down_flops)
 
 
-def call_floors(cfg, counts, S, kern):
+def call_floors(cfg, counts, S, kern, grouped_copy=False):
     """Per call of the forward pass: measured microseconds, algorithmic bytes
     (inputs read once, outputs written once, weights of active experts read
     once) and FLOPs, the floor max(bytes / HBM peak, FLOPs / matrix peak),
     and the call's fraction of its floor.  The router's FLOPs are counted as
     the three bf16 matrix passes it runs on bf16 layers (an fp32-exact
     product), against the bf16 peak; on fp32 layers as one pass against the
-    fp32 peak."""
+    fp32 peak.  Dispatch counts the grouped copy of the x rows only when
+    it makes one; otherwise the expert GEMM reads them from x itself
+    (moe_expert_ffn_gather) and dispatch moves indices only."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, H, E, N, I, K = cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K
     alg = algorithmic(cfg, counts, S)
@@ -105,8 +110,8 @@ def call_floors(cfg, counts, S, kern):
     work = {
         "moe_router_logits": (T * H * es + E * H * 4 + T * E * 4, router_flops),
         "moe_route": (T * E * 4 + E * 4 + T * K * 8 + E * 8, 0.0),
-        "moe_permute": (T * K * 4 * 2 + (N + 1) * 4 + S * 4 + T * K * 4 + T * H * es + S * H * es,
-                        0.0),
+        "moe_permute": (T * K * 4 * 2 + (N + 1) * 4 + S * 4 + T * K * 4
+                        + ((T * H * es + S * H * es) if grouped_copy else 0), 0.0),
         "moe_expert_ffn": (alg["gateup_bytes"] + alg["down_bytes"],
                            alg["gateup_flops"] + alg["down_flops"]),
         "moe_zero_experts": (T * H * es + T * H * 4 + T * K * 8, 0.0),
@@ -117,6 +122,8 @@ def call_floors(cfg, counts, S, kern):
         us = sum(kern[n][1] / kern[n][0] * 1e3 for n in names if n in kern)
         nbytes, flops = work[call]
         floor_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (mm_peak * 1e6))
+        if call == "moe_expert_ffn" and not grouped_copy:
+            call = "moe_expert_ffn_gather"
         out[call] = dict(us=round(us, 1), bytes=int(nbytes), gflop=round(flops / 1e9, 2),
                          floor_us=round(floor_us, 1),
                          frac_of_floor=round(floor_us / us, 3) if us > 0 else None)
@@ -227,7 +234,8 @@ def main():
     print(f"[bench] {cfg.name}: drawing inputs on {torch.cuda.get_device_name(dev)}",
           file=sys.stderr, flush=True)
     inp = workload.make_inputs(cfg, dev)
-    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                            grouped_copy=args.grouped_copy)
     stream = torch.cuda.current_stream(dev)
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20)
@@ -317,14 +325,15 @@ def main():
         "config": {"workload": cfg.name + ("+bias_controller" if args.bias_controller > 0 else ""),
                    "tokens": cfg.T, "hidden": cfg.H, "ffn_experts": cfg.N,
                    "zero_experts": cfg.Z, "intermediate": cfg.I, "top_k": cfg.K,
-                   "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"]},
+                   "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"],
+                   "dispatch": "grouped_copy" if args.grouped_copy else "row_gather"},
         "roofline": roofline,
         "down_gemm": {"kernel_ms": round(d_ms, 4),
                       "hbm_frac": round(alg["down_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(alg["down_flops"] / (d_ms * 1e-3) / 1e12
                                          / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()},
-        "calls": call_floors(cfg, counts, S, kern),
+        "calls": call_floors(cfg, counts, S, kern, args.grouped_copy),
         "routing": routing_stats(cfg, counts, S),
     }
     if args.flush_mib > 0:

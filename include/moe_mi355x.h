@@ -93,6 +93,8 @@ moe_status moe_route(const float *logits, const float *bias, int T, int E, int K
  * x: [T][H] (dtype); topk_idx: [T][K] with entries in [0, E); x_perm: capacity
  * [T*K][H]; row_src: capacity [T*K]; slot_row: [T*K]; offsets: [n_ffn + 1].
  * Rows >= S of x_perm and row_src are left untouched.
+ * x_perm may be NULL (and then x too): only offsets, row_src and slot_row are
+ * written, for moe_expert_ffn_gather, which reads the rows from x itself.
  * ws: device workspace of at least moe_permute_workspace_bytes(T, K, n_ffn). */
 size_t moe_permute_workspace_bytes(int T, int K, int n_ffn);
 moe_status moe_permute(const void *x, int dtype, const int32_t *topk_idx,
@@ -118,6 +120,22 @@ moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, int rows_c
                           int n_ffn, int H, int I, const void *w13, const void *w2,
                           int dtype, void *y_perm, void *ws, size_t ws_bytes,
                           void *stream);
+
+/* moe_expert_ffn with the dispatch copy folded into the first GEMM's loads
+ * (the same Key claims [§2.2] dispatch and [§2.4] experts): row r's
+ * activations are read straight from token row row_src[r] / K of x, so
+ * x_perm never needs to exist and moe_permute may be called with
+ * x_perm = NULL.  y_perm and the results are those of moe_expert_ffn on the
+ * x_perm moe_permute would have written, bit for bit.
+ * x: [T][H] (dtype, 16-byte aligned for MOE_BF16); row_src: capacity
+ * [rows_cap], as written by moe_permute, entries in [0, T*K) (others are
+ * clamped to a token row in [0, T), never read out of bounds); the other
+ * arguments, limits and errors as for moe_expert_ffn, plus MOE_ERR_SHAPE for
+ * T < 1, K < 1 or T*K >= 2^31. */
+moe_status moe_expert_ffn_gather(const void *x, int T, int K, const int32_t *row_src,
+                                 const int32_t *offsets, int rows_cap, int n_ffn, int H,
+                                 int I, const void *w13, const void *w2, int dtype,
+                                 void *y_perm, void *ws, size_t ws_bytes, void *stream);
 
 /* Zero-computation experts (Technical Report notes, Key claims [§2.1]:
  * identity experts return their input):

@@ -35,6 +35,8 @@ _SIGS = {
     "moe_permute": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_expert_ffn_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
     "moe_expert_ffn": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
+    "moe_expert_ffn_gather": ([_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P,
+                               ctypes.c_size_t, _P], _I),
     "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
     "moe_bias_update": ([_P, _I, _I, ctypes.c_float, ctypes.c_float, ctypes.c_float,
@@ -139,14 +141,19 @@ def moe_permute_workspace_bytes(T, K, n_ffn):
 
 
 def moe_permute(x, topk_idx, n_ffn, offsets, x_perm, row_src, slot_row, ws):
-    """Expert-major, token-ascending grouping of the FFN selections."""
+    """Expert-major, token-ascending grouping of the FFN selections.  With
+    x_perm None only the indices are written (for moe_expert_ffn_gather); x
+    still gives T, H and the dtype."""
     _dev(x, topk_idx, offsets, x_perm, row_src, slot_row, ws)
     T, H = x.shape
     K = topk_idx.shape[1]
-    assert x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K
+    assert topk_idx.shape[0] == T and row_src.numel() >= T * K and slot_row.numel() >= T * K
+    if x_perm is not None:
+        assert x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K
     _check("moe_permute", lib().moe_permute(
-        _ptr(x), _DT[x.dtype], _ptr(topk_idx), T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm),
-        _ptr(row_src), _ptr(slot_row), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+        _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), T, H, K, n_ffn,
+        _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(topk_idx)))
 
 
 def moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype):
@@ -164,6 +171,22 @@ def moe_expert_ffn(x_perm, offsets, w13, w2, y_perm, ws):
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(x_perm), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2), _DT[x_perm.dtype],
         _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x_perm)))
+
+
+def moe_expert_ffn_gather(x, K, row_src, offsets, w13, w2, y_perm, ws):
+    """moe_expert_ffn reading row r's activations from x[row_src[r] // K]."""
+    _dev(x, row_src, offsets, w13, w2, y_perm, ws)
+    _want(row_src, torch.int32, "row_src")
+    T, H = x.shape
+    rows_cap = y_perm.shape[0]
+    N, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H
+    assert row_src.numel() >= rows_cap
+    assert w13.dtype == w2.dtype == x.dtype == y_perm.dtype
+    _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
+        _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
+        _DT[x.dtype], _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
 
 
 def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
@@ -243,8 +266,11 @@ def moe_profile_summary() -> dict:
 
 # ------------------------------------------------------- buffers + forward --
 
-def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda"):
-    """Device buffers for one forward pass (torch allocations; no compute)."""
+def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False):
+    """Device buffers for one forward pass (torch allocations; no compute).
+    grouped_copy: also allocate x_perm [T*K, H], and forward() then copies the
+    grouped rows (moe_permute + moe_expert_ffn); by default the expert GEMM
+    gathers them from x itself (moe_expert_ffn_gather) and x_perm is None."""
     rows = T * K
     f32, i32 = torch.float32, torch.int32
     return dict(
@@ -254,7 +280,7 @@ def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda"):
         counts=torch.empty((E,), dtype=i32, device=device),
         status=torch.zeros((1,), dtype=i32, device=device),
         offsets=torch.empty((n_ffn + 1,), dtype=i32, device=device),
-        x_perm=torch.empty((rows, H), dtype=dtype, device=device),
+        x_perm=torch.empty((rows, H), dtype=dtype, device=device) if grouped_copy else None,
         row_src=torch.empty((rows,), dtype=i32, device=device),
         slot_row=torch.empty((rows,), dtype=i32, device=device),
         ws_perm=torch.empty((max(16, moe_permute_workspace_bytes(T, K, n_ffn)),),
@@ -297,13 +323,26 @@ def forward(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     with torch.cuda.stream(side):
         moe_zero_experts(x, buf["topk_idx"], buf["topk_gate"], n_ffn, buf["y_acc"])
     buf["ev_identity"].record(side)
-    moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], buf["x_perm"], buf["row_src"],
-                buf["slot_row"], buf["ws_perm"])
-    moe_expert_ffn(buf["x_perm"], buf["offsets"], w13, w2, buf["y_perm"], buf["ws_ffn"])
+    _dispatch_and_experts(x, K, n_ffn, w13, w2, buf)
     main.wait_event(buf["ev_identity"])
     moe_combine(buf["y_perm"], buf["slot_row"], buf["topk_gate"], ffn_scale, buf["y_acc"],
                 buf["y"])
     return buf["y"]
+
+
+def _dispatch_and_experts(x, K, n_ffn, w13, w2, buf):
+    """Dispatch and the FFN experts.  Without an x_perm buffer, dispatch
+    writes only the indices and the first expert GEMM loads each grouped row
+    straight from x (0.9 GB less HBM traffic on the 8192-token layer)."""
+    if buf["x_perm"] is None:
+        moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], None, buf["row_src"],
+                    buf["slot_row"], buf["ws_perm"])
+        moe_expert_ffn_gather(x, K, buf["row_src"], buf["offsets"], w13, w2, buf["y_perm"],
+                              buf["ws_ffn"])
+    else:
+        moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], buf["x_perm"], buf["row_src"],
+                    buf["slot_row"], buf["ws_perm"])
+        moe_expert_ffn(buf["x_perm"], buf["offsets"], w13, w2, buf["y_perm"], buf["ws_ffn"])
 
 
 def forward_serial(x, w_router, bias, w13, w2, K, ffn_scale, buf):
@@ -312,9 +351,7 @@ def forward_serial(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     moe_router_logits(x, w_router, buf["logits"])
     moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
               buf["status"])
-    moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], buf["x_perm"], buf["row_src"],
-                buf["slot_row"], buf["ws_perm"])
-    moe_expert_ffn(buf["x_perm"], buf["offsets"], w13, w2, buf["y_perm"], buf["ws_ffn"])
+    _dispatch_and_experts(x, K, n_ffn, w13, w2, buf)
     moe_zero_experts(x, buf["topk_idx"], buf["topk_gate"], n_ffn, buf["y_acc"])
     moe_combine(buf["y_perm"], buf["slot_row"], buf["topk_gate"], ffn_scale, buf["y_acc"],
                 buf["y"])

@@ -24,6 +24,11 @@
 //   - gate/up: weight rows are paired so that a lane holds gate column j and
 //     up column j in the same accumulator slot, and silu(g)*u is applied in
 //     registers before hh is stored (bf16);
+//   - a block's fill issues the weight halves of its first steps before the
+//     activation halves (HBM latency first; ~1 % per GEMM, measured);
+//   - gate/up can read its activation rows straight from x through row_src
+//     (the row gather): the DMA takes any 16-byte-aligned row address, so
+//     the dispatch copy into x_perm is not needed;
 //   - the output tile is staged in LDS and stored 16 bytes per lane (whole
 //     128-byte lines), not one 2-byte value per lane per instruction;
 //   - block -> tile order is XCD-aware: consecutive blocks land on the 8 XCDs
@@ -120,6 +125,8 @@ struct Ring {
 
 struct TileSrc {
   const bf16* a_rows;   // the m-tile's activation rows (see a_pitch / a_step)
+  const int32_t* gather;   // non-null: row r of the tile is row gather[r] / gK of a_rows
+  int gK, gT;              // (clamped to [0, gT)), i.e. a token row of x
   int rows;             // live rows of the m-tile
   const bf16* w;        // this expert's weight matrix (row stride KD)
   int nt, I;            // column tile, intermediate size (gate/up pairing)
@@ -139,13 +146,28 @@ __device__ __forceinline__ int weight_row(const TileSrc& t, int r) {
   return t.nt * kBN + r;
 }
 
+// Steps 0..S-2 of the loader's sweep, after the split fill: step kt's
+// activation loads have the fill's later activation loads (S - 2 - kt steps
+// of QA) and kt whole steps (Q each) behind them.  From step S - 1 on, S - 2
+// whole steps are.
+template <int S, int QA, int Q, int KT0, class F>
+__device__ __forceinline__ void ring_head(int KT, F& issue) {
+  if constexpr (KT0 < S - 1) {
+    if (KT0 >= KT) return;
+    wait_vmcnt<(S - 2 - KT0) * QA + KT0 * Q>();
+    lds_barrier();
+    issue(KT0 + S - 1);
+    ring_head<S, QA, Q, KT0 + 1>(KT, issue);
+  }
+}
+
 // Loader l (0..3) moves 8-row groups l, l+4, ... of both tiles; lane j of an
 // instruction fetches the 16-byte chunk that lands at byte 16 j of the group,
 // i.e. chunk swz(row, j & 7) of row 8 g + (j >> 3).  Every step issues the
 // same loads -- past the end they read one fixed line into a stage no one
 // reads again -- so every wait count is a constant.  The sweep starts at
 // k_start and wraps around.
-template <int G>
+template <int G, bool GATHER>
 __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD, int k_start,
                                            int l, int lane) {
   using R = Ring<G>;
@@ -153,35 +175,82 @@ __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD,
   const int KT = KD / kBK;
   const int lr = lane >> 3, lc = lane & 7;
   const bf16* src[kQ];
+  // Row gather.  Loader l's lanes need the indices of 8 G rows, 8 per group.
+  //   G <= 4: the rows of a group are wave-uniform, so the indices come in by
+  //     scalar loads (32 scalar registers at most), waited on with lgkmcnt
+  //     apart from the DMA's vmcnt, and each lane selects its row's only
+  //     after the fill's weight loads are out: the index latency hides behind
+  //     them.  A per-lane vector load would be ordered with the DMA, and the
+  //     compiler would drain every DMA before its first use.
+  //   G > 4: too many registers for that; one vector load per lane (lane j:
+  //     group j / 8, row j % 8) is waited on before any DMA is issued and
+  //     shuffled to the lanes that need it -- one round trip per block.
+  constexpr bool kScalarIdx = R::kQa <= 4;
+  int tok[R::kQa];
+  int raw[kScalarIdx ? R::kQa : 1][8];
+  if constexpr (GATHER && kScalarIdx) {
 #pragma unroll
-  for (int i = 0; i < R::kQa; ++i) {
-    const int r = (l + 4 * i) * 8 + lr;        // rows past the tile: clamped (never used)
-    src[i] = t.a_rows + (size_t)min(r, t.rows - 1) * t.a_pitch + swz(r, lc) * 8;
+    for (int i = 0; i < R::kQa; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) raw[i][j] = t.gather[min((l + 4 * i) * 8 + j, t.rows - 1)];
+  }
+  if constexpr (GATHER && !kScalarIdx) {
+    const int gi = min(lane >> 3, R::kQa - 1);
+    const int v = t.gather[min((l + 4 * gi) * 8 + (lane & 7), t.rows - 1)];
+#pragma unroll
+    for (int i = 0; i < R::kQa; ++i) tok[i] = __shfl(v, i * 8 + lr);
+    __builtin_amdgcn_sched_barrier(0);   // no DMA may be moved above that wait
   }
 #pragma unroll
   for (int i = 0; i < R::kQb; ++i) {
     const int r = (l + 4 * i) * 8 + lr;
     src[R::kQa + i] = t.w + (size_t)weight_row(t, r) * KD + swz(r, lc) * 8;
   }
-  auto issue = [&](int kt) {
-    char* sb = smem + (kt % S) * R::kStageBytes;
+  auto stage = [&](int kt) { return smem + (kt % S) * R::kStageBytes; };
+  auto k_of = [&](int kt) { const int ks = kt + k_start; return ks >= KT ? ks - KT : ks; };
+  auto issue_a = [&](int kt) {
     const bool real = kt < KT;
-    int ks = kt + k_start;
-    ks = ks >= KT ? ks - KT : ks;
-    const int k0 = real ? ks * kBK : 0;
-    const size_t ka = real ? (size_t)ks * t.a_step : 0;
+    const size_t ka = real ? (size_t)k_of(kt) * t.a_step : 0;
 #pragma unroll
     for (int i = 0; i < R::kQa; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(real ? src[i] + ka : t.w),
-                                       (lds_void*)(sb + (l + 4 * i) * 1024), 16, 0, 0);
+                                       (lds_void*)(stage(kt) + (l + 4 * i) * 1024), 16, 0, 0);
+  };
+  auto issue_b = [&](int kt) {
+    const bool real = kt < KT;
+    const int k0 = real ? k_of(kt) * kBK : 0;
 #pragma unroll
     for (int i = 0; i < R::kQb; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(real ? src[R::kQa + i] + k0 : t.w),
-                                       (lds_void*)(sb + R::kABytes + (l + 4 * i) * 1024), 16,
-                                       0, kCachePolicyNT);
+                                       (lds_void*)(stage(kt) + R::kABytes + (l + 4 * i) * 1024),
+                                       16, 0, kCachePolicyNT);
   };
-  for (int kt = 0; kt < S - 1; ++kt) issue(kt);
-  for (int kt = 0; kt < KT; ++kt) {
+  auto issue = [&](int kt) {
+    issue_a(kt);
+    issue_b(kt);
+  };
+  // Fill: the weight halves of the first S - 1 steps go out first (HBM, the
+  // longest wait), then their activation halves, whose addresses may still be
+  // waiting on the row-gather index loads.
+  for (int kt = 0; kt < S - 1; ++kt) issue_b(kt);
+  if constexpr (GATHER && kScalarIdx) {
+#pragma unroll
+    for (int i = 0; i < R::kQa; ++i) {
+      int v = raw[i][0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) v = lr == j ? raw[i][j] : v;
+      tok[i] = v;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R::kQa; ++i) {
+    const int r = (l + 4 * i) * 8 + lr;        // rows past the tile: clamped (never used)
+    const int ar = GATHER ? min(max(tok[i], 0) / t.gK, t.gT - 1) : min(r, t.rows - 1);
+    src[i] = t.a_rows + (size_t)ar * t.a_pitch + swz(r, lc) * 8;
+  }
+  for (int kt = 0; kt < S - 1; ++kt) issue_a(kt);
+  ring_head<S, R::kQa, kQ, 0>(KT, issue);
+  for (int kt = S - 1; kt < KT; ++kt) {
     wait_vmcnt<(S - 2) * kQ>();   // step kt has landed (in-order completion)
     lds_barrier();                // publish step kt; every wave is done with step kt - 1
     issue(kt + S - 1);            // into the stage step kt - 1 used
@@ -296,8 +365,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, const int4* __restrict__ tiles,
-    const int* __restrict__ ntiles, int KD, int I, int H, int NT, bf16* __restrict__ C) {
+    const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
+    const bf16* __restrict__ W, const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+    int KD, int I, int H, int NT, bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
   static_assert(BM == 256, "instances cover 8 groups of 32 rows");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -313,10 +383,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
 
   const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
-  // Activation rows: x_perm is row-major [rows][H]; hh is m-tile-blocked:
-  // rows [row0, row0 + rows) of column block j (64 columns, one K step of
-  // the down GEMM) sit contiguously at row0 * I + j * rows * 64.
-  const TileSrc src{A + (size_t)row0 * KD, rows, W + (size_t)e * wrows * KD, nt, I, GATEUP,
+  // Activation rows: x_perm is row-major [rows][H], or (gather) the rows are
+  // token rows of x picked through row_src, each a contiguous 2H-byte row all
+  // the same, so the DMA loads them in place and no grouped copy is made; hh
+  // is m-tile-blocked: rows [row0, row0 + rows) of column block j (64
+  // columns, one K step of the down GEMM) sit contiguously at
+  // row0 * I + j * rows * 64.
+  const TileSrc src{gather ? A : A + (size_t)row0 * KD, gather ? gather + row0 : nullptr, gK, gT,
+                    rows, W + (size_t)e * wrows * KD, nt, I, GATEUP,
                     GATEUP ? KD : kBK, GATEUP ? kBK : rows * kBK};
   // The column tiles of one m-tile run side by side on one XCD and read the
   // same activation rows.  Swept in lockstep, every one of them waits on the
@@ -337,7 +411,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   if (wave >= 4) {   // loader waves
     switch (groups) {
 #define MOE_CASE(g) \
-      case g: ffn_loader<g>(smem, src, KD, k_start, wave - 4, lane); break;
+      case g:                                                                  \
+        if (GATEUP && src.gather)                                              \
+          ffn_loader<g, GATEUP>(smem, src, KD, k_start, wave - 4, lane);       \
+        else                                                                   \
+          ffn_loader<g, false>(smem, src, KD, k_start, wave - 4, lane);        \
+        break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
       MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
@@ -425,6 +504,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 // accumulation); any H and I.  Tile: 32 rows x 32 outputs, K step 32.
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads) void ffn_f32(const float* __restrict__ A,
+                                                    const int32_t* __restrict__ gather, int gK,
+                                                    int gT,
                                                     const float* __restrict__ W,
                                                     const int4* __restrict__ tiles,
                                                     const int* __restrict__ ntiles, int KD, int I,
@@ -446,7 +527,12 @@ __global__ __launch_bounds__(kThreads) void ffn_f32(const float* __restrict__ A,
   for (int k0 = 0; k0 < KD; k0 += TK) {
     for (int i = threadIdx.x; i < TM * TK; i += kThreads) {
       const int r = i / TK, k = i % TK;
-      As[k][r] = (r < rows && k0 + k < KD) ? A[(size_t)(row0 + r) * KD + k0 + k] : 0.0f;
+      if (r < rows && k0 + k < KD) {
+        const int ar = gather ? min(max(gather[row0 + r], 0) / gK, gT - 1) : row0 + r;
+        As[k][r] = A[(size_t)ar * KD + k0 + k];
+      } else {
+        As[k][r] = 0.0f;
+      }
     }
     for (int i = threadIdx.x; i < NB * TK; i += kThreads) {
       const int c = i / TK, k = i % TK;
@@ -492,9 +578,10 @@ size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype) {
          align256((size_t)rows_cap * I * es);
 }
 
-hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
-                             int H, int I, const void* w13, const void* w2, int dtype,
-                             void* y_perm, void* ws, hipStream_t s) {
+hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, int gT,
+                             const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
+                             const void* w13, const void* w2, int dtype, void* y_perm, void* ws,
+                             hipStream_t s) {
   const int bm = ffn_bm(dtype);
   const size_t mtmax = max_mtiles(rows_cap, n_ffn, bm);
   int* ntiles = (int*)ws;
@@ -508,20 +595,22 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int row
     const int nt1 = I / 64, nt2 = H / kBN;
     MOE_LAUNCH("ffn_gateup_bf16", s,
                ffn_mfma_bf16<true><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
-                   (const bf16*)x_perm, (const bf16*)w13, tiles, ntiles, H, I, H, nt1,
-                   (bf16*)hh));
+                   (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
+                   H, nt1, (bf16*)hh));
     MOE_LAUNCH("ffn_down_bf16", s,
                ffn_mfma_bf16<false><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
-                   (const bf16*)hh, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
-                   (bf16*)y_perm));
+                   (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
+                   nt2, (bf16*)y_perm));
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
     MOE_LAUNCH("ffn_gateup_f32", s,
-               ffn_f32<true><<<g1, kThreads, 0, s>>>((const float*)x_perm, (const float*)w13,
-                                                     tiles, ntiles, H, I, H, (float*)hh));
+               ffn_f32<true><<<g1, kThreads, 0, s>>>((const float*)x_perm, gather, gK, gT,
+                                                     (const float*)w13, tiles, ntiles, H, I, H,
+                                                     (float*)hh));
     MOE_LAUNCH("ffn_down_f32", s,
-               ffn_f32<false><<<g2, kThreads, 0, s>>>((const float*)hh, (const float*)w2, tiles,
-                                                      ntiles, I, I, H, (float*)y_perm));
+               ffn_f32<false><<<g2, kThreads, 0, s>>>((const float*)hh, nullptr, 1, 1,
+                                                      (const float*)w2, tiles, ntiles, I, I, H,
+                                                      (float*)y_perm));
   }
   return hipGetLastError();
 }

@@ -68,7 +68,8 @@ size_t moe_permute_workspace_bytes(int T, int K, int n_ffn) {
 moe_status moe_permute(const void* x, int dtype, const int32_t* topk_idx, int T, int H, int K,
                        int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
                        int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !topk_idx || !offsets || !x_perm || !row_src || !slot_row || !ws) return MOE_ERR_NULL;
+  if ((x_perm && !x) || !topk_idx || !offsets || !row_src || !slot_row || !ws)
+    return MOE_ERR_NULL;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
   if (T < 1 || H < 1 || H % 8 || K < 1 || n_ffn < 0 || n_ffn > kMaxFfn ||
       !fits_i32((long long)T * K))
@@ -86,22 +87,48 @@ size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype)
   return ffn_ws_bytes(rows_cap, n_ffn, I, dtype);
 }
 
-moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
-                          int H, int I, const void* w13, const void* w2, int dtype, void* y_perm,
-                          void* ws, size_t ws_bytes, void* stream) {
-  if (!x_perm || !offsets || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_NULL;
+namespace {
+// The checks both expert-FFN entry points share; a is the activation source.
+moe_status ffn_checks(const void* a, const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
+                      const void* w13, const void* w2, int dtype, const void* y_perm,
+                      const void* ws, size_t ws_bytes) {
+  if (!a || !offsets || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_NULL;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
   if (rows_cap < 1 || n_ffn < 0 || n_ffn > kMaxFfn || H < 1 || I < 1) return MOE_ERR_SHAPE;
   if (dtype == MOE_BF16 && (H % 128 || I % 64)) return MOE_ERR_SHAPE;
   if (dtype == MOE_F32 && (long long)rows_cap / 32 + n_ffn + 8 > 65535) return MOE_ERR_SHAPE;
-  const size_t a = dtype == MOE_BF16 ? 16 : 4;
-  if (!aligned(x_perm, a) || !aligned(w13, a) || !aligned(w2, a) || !aligned(y_perm, a) ||
+  const size_t al = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(a, al) || !aligned(w13, al) || !aligned(w2, al) || !aligned(y_perm, al) ||
       !aligned(offsets, 4) || !aligned(ws, 256))
     return MOE_ERR_ALIGN;
   if (ws_bytes < ffn_ws_bytes(rows_cap, n_ffn, I, dtype)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
+                          int H, int I, const void* w13, const void* w2, int dtype, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st =
+      ffn_checks(x_perm, offsets, rows_cap, n_ffn, H, I, w13, w2, dtype, y_perm, ws, ws_bytes);
+  if (st != MOE_OK || n_ffn == 0) return st;
+  return launched(launch_expert_ffn(x_perm, nullptr, 1, 1, offsets, rows_cap, n_ffn, H, I, w13,
+                                    w2, dtype, y_perm, ws, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_gather(const void* x, int T, int K, const int32_t* row_src,
+                                 const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
+                                 const void* w13, const void* w2, int dtype, void* y_perm,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!row_src) return MOE_ERR_NULL;
+  const moe_status st =
+      ffn_checks(x, offsets, rows_cap, n_ffn, H, I, w13, w2, dtype, y_perm, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (T < 1 || K < 1 || !fits_i32((long long)T * K)) return MOE_ERR_SHAPE;
+  if (!aligned(row_src, 4)) return MOE_ERR_ALIGN;
   if (n_ffn == 0) return MOE_OK;
-  return launched(launch_expert_ffn(x_perm, offsets, rows_cap, n_ffn, H, I, w13, w2, dtype, y_perm,
-                                    ws, (hipStream_t)stream));
+  return launched(launch_expert_ffn(x, row_src, K, T, offsets, rows_cap, n_ffn, H, I, w13, w2,
+                                    dtype, y_perm, ws, (hipStream_t)stream));
 }
 
 moe_status moe_zero_experts(const void* x, int dtype, const int32_t* topk_idx,

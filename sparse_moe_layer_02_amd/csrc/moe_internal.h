@@ -70,9 +70,12 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, i
                           int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
                           int32_t* slot_row, void* ws, hipStream_t s);
 size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype);
-hipError_t launch_expert_ffn(const void* x_perm, const int32_t* offsets, int rows_cap, int n_ffn,
-                             int H, int I, const void* w13, const void* w2, int dtype,
-                             void* y_perm, void* ws, hipStream_t s);
+// gather == nullptr: row r's activations are x_perm[r]; otherwise they are
+// token row gather[r] / gK (clamped to [0, gT)) of x_perm, i.e. of x.
+hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, int gT,
+                             const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
+                             const void* w13, const void* w2, int dtype, void* y_perm, void* ws,
+                             hipStream_t s);
 hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, const float* gate,
                                int T, int H, int K, int n_ffn, float* y_acc, hipStream_t s);
 hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row,

@@ -10,8 +10,8 @@
 //     cnt[e][b]                      = popcount(mask[e]).
 //   row(t, e) = offsets[e] + sum_{b' < b} cnt[e][b'] + rank.
 // Kernels: hist (cnt), scan over blocks per expert, scan over experts
-// (offsets), scatter (slot_row, row_src), gather (x rows, one read of x[t]
-// feeding all of its rows).
+// (offsets), scatter (slot_row, row_src), and, when a grouped copy is asked
+// for, gather (x rows, one read of x[t] feeding all of its rows).
 #include "moe_internal.h"
 
 namespace moe {
@@ -190,6 +190,7 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, i
   MOE_LAUNCH("permute_scatter", s,
              perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets,
                                                    row_src, slot_row));
+  if (!x_perm) return hipGetLastError();   // indices only: the GEMM gathers x rows itself
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = (int)((size_t)H * esize / 16);
   if (row_vecs <= 256 * 4)

@@ -112,10 +112,15 @@ def stage_checks(cfg, inp, buf, ffn_experts=None):
     np.testing.assert_array_equal(host(buf["offsets"]), off_ref)
     np.testing.assert_array_equal(host(buf["row_src"])[:S], row_src_ref)
     np.testing.assert_array_equal(host(buf["slot_row"]), slot_ref)
-    rs = torch.from_numpy(row_src_ref.astype(np.int64)).to(inp["x"].device)
-    assert torch.equal(buf["x_perm"][:S], inp["x"][rs // K])
+    if buf["x_perm"] is not None:
+        # grouped copy: the rows are bit copies of x; the FFN is fed that copy
+        rs = torch.from_numpy(row_src_ref.astype(np.int64)).to(inp["x"].device)
+        assert torch.equal(buf["x_perm"][:S], inp["x"][rs // K])
+        xp = host(buf["x_perm"][:S])
+    else:
+        # row gather: the FFN read x[row_src // K] itself (row_src checked above)
+        xp = x[row_src_ref // K]
     # S3 FFN rows on identical grouped rows
-    xp = host(buf["x_perm"][:S])
     yp = host(buf["y_perm"][:S])
     experts = range(N) if ffn_experts is None else ffn_experts
     errs = []

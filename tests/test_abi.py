@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -89,6 +89,13 @@ def test_permute_validation():
     assert f(*a) == WS
     a = list(args); a[8] = P(0x10008)             # x_perm not 16-byte aligned
     assert f(*a) == ALIGN
+    a = list(args); a[0] = None                   # x without x_perm to copy into
+    assert f(*a) == NULL
+    a = list(args); a[0] = None; a[8] = None      # indices only (no copy): x unused
+    a[6] = 5000
+    assert f(*a) == SHAPE                         # still validated past the NULL check
+    a = list(args); a[9] = None                   # row_src is always written
+    assert f(*a) == NULL
 
 
 def test_expert_ffn_validation():
@@ -106,6 +113,32 @@ def test_expert_ffn_validation():
     a = list(args); a[8] = 9
     assert f(*a) == DTYPE
     a = list(args); a[3] = 0                      # no FFN experts: nothing to do
+    assert f(*a) == OK
+
+
+def test_expert_ffn_gather_validation():
+    f = moe.lib().moe_expert_ffn_gather
+    need = moe.lib().moe_expert_ffn_workspace_bytes(256, 16, 1024, 1)
+    args = [FAKE, 64, 4, FAKE, FAKE, 256, 16, 2048, 1024, FAKE, FAKE, 1, FAKE, FAKE, need, None]
+    a = list(args); a[3] = None                   # row_src
+    assert f(*a) == NULL
+    a = list(args); a[0] = None                   # x
+    assert f(*a) == NULL
+    a = list(args); a[1] = 0                      # T
+    assert f(*a) == SHAPE
+    a = list(args); a[2] = 0                      # K
+    assert f(*a) == SHAPE
+    a = list(args); a[1] = 1 << 28; a[2] = 8      # T*K >= 2^31
+    assert f(*a) == SHAPE
+    a = list(args); a[7] = 2000                   # bf16 path needs H % 128 == 0
+    assert f(*a) == SHAPE
+    a = list(args); a[0] = P(0x10008)             # x rows not 16-byte aligned
+    assert f(*a) == ALIGN
+    a = list(args); a[3] = P(0x10002)             # row_src not int-aligned
+    assert f(*a) == ALIGN
+    a = list(args); a[14] = need - 1
+    assert f(*a) == WS
+    a = list(args); a[6] = 0                      # no FFN experts: nothing to do
     assert f(*a) == OK
 
 

@@ -80,7 +80,7 @@ def test_full_scale_layer(name, shared_weights):
     np.testing.assert_array_equal(host(buf["row_src"][:S]), rs_ref)
     np.testing.assert_array_equal(host(buf["slot_row"]), slot_ref)
     rs = torch.from_numpy(rs_ref.astype(np.int64)).to(dev)
-    assert torch.equal(buf["x_perm"][:S], x_t[rs // K])
+    assert buf["x_perm"] is None    # the expert GEMM gathers x[row_src // K] itself
 
     # S3: FFN rows of sampled experts on the GPU's grouped rows
     ffn_counts = counts[:N]
@@ -95,7 +95,7 @@ def test_full_scale_layer(name, shared_weights):
                                                             rng.choice(m, 16, False)])
         w13e, w2e = _expert_host(w13, w2, int(e))
         sel = torch.from_numpy((a + rows).astype(np.int64)).to(dev)
-        ref = oracle.ffn_rows(host(buf["x_perm"][sel]), w13e, w2e, threads=THREADS)
+        ref = oracle.ffn_rows(host(x_t[rs[sel] // K]), w13e, w2e, threads=THREADS)
         err = normwise(host(buf["y_perm"][sel]), ref)
         print(f"  expert {int(e)} ({m} rows): y_perm normwise {err:.3e}", flush=True)
         e3 = max(e3, err)

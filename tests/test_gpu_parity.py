@@ -14,13 +14,14 @@ from _parity import (TOL, check_end_to_end, device, forward, host, inputs_on_hos
 pytestmark = pytest.mark.gpu
 
 
-def _run(cfg, bias=None):
+def _run(cfg, bias=None, grouped_copy=False):
     dev = device()
-    print(f"\n[case] {cfg}", flush=True)
+    print(f"\n[case] {cfg} grouped_copy={grouped_copy}", flush=True)
     inp = workload.make_inputs(cfg, dev)
     if bias is not None:
         inp["bias"] = torch.as_tensor(bias, dtype=torch.float32, device=dev)
-    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                            grouped_copy=grouped_copy)
     forward(cfg, inp, buf)
     return inp, buf
 
@@ -34,16 +35,20 @@ def _e2e(cfg, inp, buf, tokens=None):
     return err
 
 
-def test_tiny_fp32_layer():
+# grouped_copy: dispatch copies the rows (moe_permute + moe_expert_ffn);
+# otherwise the expert GEMM gathers them from x (moe_expert_ffn_gather).
+@pytest.mark.parametrize("grouped_copy", [False, True])
+def test_tiny_fp32_layer(grouped_copy):
     cfg = workload.CONFIGS["tiny_fp32"]
-    inp, buf = _run(cfg)
+    inp, buf = _run(cfg, grouped_copy=grouped_copy)
     print(stage_checks(cfg, inp, buf))
     _e2e(cfg, inp, buf)
 
 
-def test_mid_bf16_layer():
+@pytest.mark.parametrize("grouped_copy", [False, True])
+def test_mid_bf16_layer(grouped_copy):
     cfg = workload.CONFIGS["mid_bf16"]
-    inp, buf = _run(cfg)
+    inp, buf = _run(cfg, grouped_copy=grouped_copy)
     counts = host(buf["counts"])[:cfg.N]
     order = np.argsort(counts)
     experts = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
@@ -176,18 +181,22 @@ def test_forward_is_bitwise_deterministic():
     assert torch.equal(buf["y_perm"][:S], yp1[:S])
 
 
-def test_rows_past_the_grouped_rows_are_untouched():
+@pytest.mark.parametrize("grouped_copy", [False, True])
+def test_rows_past_the_grouped_rows_are_untouched(grouped_copy):
     cfg = workload.CONFIGS["tiny_fp32"].replace(T=100)
     dev = device()
     inp = workload.make_inputs(cfg, dev)
-    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
-    buf["x_perm"].fill_(123.0)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                            grouped_copy=grouped_copy)
+    if grouped_copy:
+        buf["x_perm"].fill_(123.0)
     buf["y_perm"].fill_(-7.0)
     buf["row_src"].fill_(-5)
     forward(cfg, inp, buf)
     S = int(host(buf["offsets"])[-1])
     assert S < cfg.T * cfg.K
-    assert (host(buf["x_perm"][S:]) == 123.0).all()
+    if grouped_copy:
+        assert (host(buf["x_perm"][S:]) == 123.0).all()
     assert (host(buf["y_perm"][S:]) == -7.0).all()
     assert (host(buf["row_src"][S:]) == -5).all()
 
@@ -237,3 +246,63 @@ def test_two_stream_forward_matches_serial():
             torch.cuda.synchronize()
             assert torch.equal(got, ref[i])
     assert not torch.equal(ref[0], ref[1])
+
+
+@pytest.mark.parametrize("name,T,heavy", [("tiny_fp32", None, None), ("mid_bf16", 1500, None),
+                                          ("mid_bf16", 1200, (3,))])
+def test_row_gather_matches_grouped_copy(name, T, heavy):
+    # The expert GEMM reading x[row_src // K] must give the same bits as the
+    # GEMM on the grouped copy: same rows, same kernels, same order.  The
+    # third case sends ~1100 rows to one expert (full 256-row tiles).
+    cfg = workload.CONFIGS[name]
+    if T is not None:
+        cfg = cfg.replace(T=T)
+    dev = device()
+    inp = workload.make_inputs(cfg, dev)
+    if heavy is not None:
+        bias = np.zeros(cfg.E, np.float32)
+        bias[list(heavy)] = 4.0
+        inp["bias"] = torch.as_tensor(bias, device=dev)
+    out = {}
+    for copy in (True, False):
+        buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                                grouped_copy=copy)
+        forward(cfg, inp, buf)
+        S = int(host(buf["offsets"])[-1])
+        out[copy] = (buf["y_perm"][:S].clone(), buf["y"].clone(), host(buf["counts"]))
+    if heavy is not None:
+        assert out[True][2][heavy[0]] > 4 * 256
+    assert torch.equal(out[True][0], out[False][0])
+    assert torch.equal(out[True][1], out[False][1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_row_gather_clamps_out_of_range_sources(dtype):
+    # row_src entries outside [0, T*K) read a clamped token row of x, never
+    # past it: compare with moe_expert_ffn on x_perm built from the same
+    # clamped rows.
+    T, K, H, I, N = 40, 3, 256, 128, 4
+    dev = device()
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cpu").manual_seed(5)
+    x = torch.randn(T, H, generator=g).to(td).to(dev)
+    w13 = (torch.randn(N, 2 * I, H, generator=g) * 0.05).to(td).to(dev)
+    w2 = (torch.randn(N, H, I, generator=g) * 0.05).to(td).to(dev)
+    rows_cap = T * K
+    S = 90
+    offsets = torch.tensor([0, 30, 30, 75, S], dtype=torch.int32, device=dev)
+    rs = torch.randint(0, T * K, (rows_cap,), generator=g, dtype=torch.int32)
+    rs[[0, 7, 31, 60, 89]] = torch.tensor([-1, -(2 ** 31), T * K, 2 ** 31 - 1, T * K + 5],
+                                          dtype=torch.int32)
+    tok = (rs.clamp(min=0).long() // K).clamp(max=T - 1)
+    rs = rs.to(dev)
+    x_perm = x[tok.to(dev)].contiguous()
+    ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(rows_cap, N, I, td), dtype=torch.uint8,
+                     device=dev)
+    y_ref = torch.zeros(rows_cap, H, dtype=td, device=dev)
+    y_got = torch.zeros(rows_cap, H, dtype=td, device=dev)
+    moe.moe_expert_ffn(x_perm, offsets, w13, w2, y_ref, ws)
+    moe.moe_expert_ffn_gather(x, K, rs, offsets, w13, w2, y_got, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_got[:S], y_ref[:S])
+    assert (host(y_got[S:]) == 0).all()
