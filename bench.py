@@ -1,8 +1,10 @@
 """Benchmark of the MoE layer forward pass on one MI355X.
 
-One step = the six calls of one forward pass (router scores, routing,
-dispatch, expert FFNs, identity experts, combine) over one batch of synthetic
-input already resident in HBM, enqueued back to back on one stream.  Default
+One step = one forward pass over one batch of synthetic input already
+resident in HBM, enqueued back to back on one stream: router scores, routing,
+dispatch (indices), the expert FFNs (gathering their rows from x), and combine
+with the identity experts' term folded in (--grouped-copy and
+--separate-identity time the six-call composition's pieces instead).  Default
 workload: the full-scale prefill-shaped layer (T = 8192 tokens, hidden 6144,
 512 SwiGLU FFN experts of intermediate 2048 + 256 identity experts, K = 12,
 38.65 GB of bf16 expert weights on the GPU).
@@ -47,6 +49,7 @@ CALLS = {
                        "ffn_down_dense_bf16", "ffn_gateup_f32", "ffn_down_f32"),
     "moe_zero_experts": ("zero_experts",),
     "moe_combine": ("combine",),
+    "moe_combine_identity": ("combine_identity",),
 }
 METRIC = "MoE-layer tokens/sec at 1 GPU; grouped-GEMM MFMA util and HBM GB/s vs peak"
 
@@ -70,6 +73,10 @@ def parse():
     p.add_argument("--grouped-copy", action="store_true",
                    help="dispatch copies the grouped x rows (moe_permute into x_perm, then "
                         "moe_expert_ffn) instead of the expert GEMM gathering them from x")
+    p.add_argument("--separate-identity", action="store_true",
+                   help="run the identity experts as their own call (moe_zero_experts into "
+                        "y_acc, on a second stream, then moe_combine) instead of inside combine "
+                        "(moe_combine_identity)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -116,9 +123,12 @@ def call_floors(cfg, counts, S, kern, grouped_copy=False):
                            alg["gateup_flops"] + alg["down_flops"]),
         "moe_zero_experts": (T * H * es + T * H * 4 + T * K * 8, 0.0),
         "moe_combine": (S * H * es + T * H * 4 + T * H * es + T * K * 8, 0.0),
+        "moe_combine_identity": (S * H * es + T * H * es + T * H * es + T * K * 8, 0.0),
     }
     out = {}
     for call, names in CALLS.items():
+        if not any(n in kern for n in names):
+            continue      # not a call of this forward path
         us = sum(kern[n][1] / kern[n][0] * 1e3 for n in names if n in kern)
         nbytes, flops = work[call]
         floor_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (mm_peak * 1e6))
@@ -235,7 +245,8 @@ def main():
           file=sys.stderr, flush=True)
     inp = workload.make_inputs(cfg, dev)
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
-                            grouped_copy=args.grouped_copy)
+                            grouped_copy=args.grouped_copy,
+                            separate_identity=args.separate_identity)
     stream = torch.cuda.current_stream(dev)
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20)
@@ -326,7 +337,8 @@ def main():
                    "tokens": cfg.T, "hidden": cfg.H, "ffn_experts": cfg.N,
                    "zero_experts": cfg.Z, "intermediate": cfg.I, "top_k": cfg.K,
                    "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"],
-                   "dispatch": "grouped_copy" if args.grouped_copy else "row_gather"},
+                   "dispatch": "grouped_copy" if args.grouped_copy else "row_gather",
+                   "identity_experts": "separate" if args.separate_identity else "in_combine"},
         "roofline": roofline,
         "down_gemm": {"kernel_ms": round(d_ms, 4),
                       "hbm_frac": round(alg["down_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

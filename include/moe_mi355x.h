@@ -156,6 +156,23 @@ moe_status moe_combine(const void *y_perm, int dtype, const int32_t *slot_row,
                        const float *topk_gate, float ffn_scale, const float *y_acc,
                        int T, int H, int K, void *y, void *stream);
 
+/* moe_zero_experts and moe_combine in one pass (the same Key claims [§2.1]
+ * identity experts, [§2.2] combine, [§2.3.2 Eq. 8] compensation):
+ *   y[t] = (sum over slots k with slot_row < 0, in slot order, of
+ *           topk_gate[t][k]) * x[t]
+ *        + sum over slots k with slot_row >= 0, in slot order, of
+ *          (ffn_scale * topk_gate[t][k]) * y_perm[slot_row[t*K + k]]
+ * in fp32, stored in dtype.  The identity slots are the ones moe_permute
+ * marks -1, i.e. the picks of experts >= n_ffn.  The fp32 operations and
+ * their order are those of the two calls, so y is bitwise the same; y_acc is
+ * neither needed nor written (4H bytes per token less each way).
+ * x: [T][H] (dtype); y_perm, slot_row, topk_gate, y, limits and errors as for
+ * moe_combine. */
+moe_status moe_combine_identity(const void *y_perm, const void *x, int dtype,
+                                const int32_t *slot_row, const float *topk_gate,
+                                float ffn_scale, int T, int H, int K, void *y,
+                                void *stream);
+
 /* Bias controller (Technical Report notes, Key claims [§2.1.1, §2.1.2] and
  * Method: each FFN expert's selection bias is adjusted from token-routing
  * frequency by a PID controller so that the average number of activated FFN

@@ -39,6 +39,7 @@ _SIGS = {
                                ctypes.c_size_t, _P], _I),
     "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
+    "moe_combine_identity": ([_P, _P, _I, _P, _P, ctypes.c_float, _I, _I, _I, _P, _P], _I),
     "moe_bias_update": ([_P, _I, _I, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                          ctypes.c_float, _P, _P, _P, _P], _I),
     "moe_router_similarity_workspace_bytes": ([_I, _I], ctypes.c_size_t),
@@ -211,6 +212,20 @@ def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
         _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
 
 
+def moe_combine_identity(y_perm, x, slot_row, topk_gate, ffn_scale, y):
+    """moe_zero_experts + moe_combine in one pass: y = (sum of the identity
+    slots' gates) * x + sum of ffn_scale * gate * y_perm rows, in slot order."""
+    _dev(y_perm, x, slot_row, topk_gate, y)
+    T, H = y.shape
+    K = topk_gate.shape[1]
+    assert x.shape == (T, H) and y_perm.shape[1] == H and topk_gate.shape[0] == T
+    assert slot_row.numel() >= T * K
+    assert y_perm.dtype == x.dtype == y.dtype
+    _check("moe_combine_identity", lib().moe_combine_identity(
+        _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
+        T, H, K, _ptr(y), _stream(y)))
+
+
 def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_err):
     """One PID update of the FFN experts' selection bias from a batch's counts."""
     _dev(counts, bias, integral, prev_err)
@@ -266,11 +281,16 @@ def moe_profile_summary() -> dict:
 
 # ------------------------------------------------------- buffers + forward --
 
-def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False):
+def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False,
+                  separate_identity=False):
     """Device buffers for one forward pass (torch allocations; no compute).
     grouped_copy: also allocate x_perm [T*K, H], and forward() then copies the
     grouped rows (moe_permute + moe_expert_ffn); by default the expert GEMM
-    gathers them from x itself (moe_expert_ffn_gather) and x_perm is None."""
+    gathers them from x itself (moe_expert_ffn_gather) and x_perm is None.
+    separate_identity: also allocate y_acc [T, H] fp32, and forward() runs the
+    identity experts as their own call (moe_zero_experts, then moe_combine);
+    by default combine computes their term itself (moe_combine_identity) and
+    y_acc is None.  Both options give bitwise the same y."""
     rows = T * K
     f32, i32 = torch.float32, torch.int32
     return dict(
@@ -288,13 +308,13 @@ def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False
         y_perm=torch.empty((rows, H), dtype=dtype, device=device),
         ws_ffn=torch.empty((max(256, moe_expert_ffn_workspace_bytes(rows, n_ffn, I, dtype)),),
                            dtype=torch.uint8, device=device),
-        y_acc=torch.empty((T, H), dtype=f32, device=device),
+        y_acc=torch.empty((T, H), dtype=f32, device=device) if separate_identity else None,
         y=torch.empty((T, H), dtype=dtype, device=device),
-        # a second stream (default priority) for the identity experts, and
-        # the two events that order it against the current stream
-        side_stream=torch.cuda.Stream(device=device),
-        ev_routed=torch.cuda.Event(),
-        ev_identity=torch.cuda.Event(),
+        # six-call path: a second stream (default priority) for the identity
+        # experts, and the two events that order it against the current stream
+        side_stream=torch.cuda.Stream(device=device) if separate_identity else None,
+        ev_routed=torch.cuda.Event() if separate_identity else None,
+        ev_identity=torch.cuda.Event() if separate_identity else None,
     )
 
 
@@ -302,6 +322,28 @@ OVERLAP_MIN_TOKENS = 1024
 
 
 def forward(x, w_router, bias, w13, w2, K, ffn_scale, buf):
+    """One layer forward on the current stream, no host synchronisation.
+    With the default buffers: router, routing, dispatch (indices only), the
+    expert GEMMs gathering their rows from x, and combine with the identity
+    experts' term folded in -- five calls.  With separate_identity buffers,
+    the six calls of _forward_six."""
+    if buf["y_acc"] is None:
+        return _forward_fused(x, w_router, bias, w13, w2, K, ffn_scale, buf)
+    return _forward_six(x, w_router, bias, w13, w2, K, ffn_scale, buf)
+
+
+def _forward_fused(x, w_router, bias, w13, w2, K, ffn_scale, buf):
+    n_ffn = w13.shape[0]
+    moe_router_logits(x, w_router, buf["logits"])
+    moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
+              buf["status"])
+    _dispatch_and_experts(x, K, n_ffn, w13, w2, buf)
+    moe_combine_identity(buf["y_perm"], x, buf["slot_row"], buf["topk_gate"], ffn_scale,
+                         buf["y"])
+    return buf["y"]
+
+
+def _forward_six(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     """The six calls of one layer forward, enqueued on the current stream with
     no host synchronisation.  The identity experts depend only on the routing,
     so for batches of OVERLAP_MIN_TOKENS tokens or more they run on a second
@@ -346,7 +388,10 @@ def _dispatch_and_experts(x, K, n_ffn, w13, w2, buf):
 
 
 def forward_serial(x, w_router, bias, w13, w2, K, ffn_scale, buf):
-    """The same six calls, all on the current stream in layer order."""
+    """forward() with every call on the current stream in layer order (the
+    six-call path does not use its second stream)."""
+    if buf["y_acc"] is None:
+        return _forward_fused(x, w_router, bias, w13, w2, K, ffn_scale, buf)
     n_ffn = w13.shape[0]
     moe_router_logits(x, w_router, buf["logits"])
     moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],

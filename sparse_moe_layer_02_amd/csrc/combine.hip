@@ -74,45 +74,82 @@ __global__ __launch_bounds__(kMaxThreads) void zero_experts_kernel(
   }
 }
 
-// y[t] = y_acc[t] + sum over FFN slots (in slot order) of (scale*gate) * y_perm[row]
-template <typename T>
+// The token's slot list, read by wave 0 (64 slots per step, one lane each):
+// the FFN slots' rows and weights (scale * gate), compacted in slot order into
+// LDS, and the sum of the identity slots' gates (slot_row < 0), added in slot
+// order on every lane -- the same fp32 order as zero_experts_kernel.
+struct SlotList {
+  int rows[kMaxK];
+  float wts[kMaxK];
+  int n;
+  float identity_gate;
+};
+
+__device__ __forceinline__ void read_slots(SlotList& sl, const int32_t* __restrict__ slot_row,
+                                           const float* __restrict__ gate, float scale, int K,
+                                           int t) {
+  const int lane = threadIdx.x;
+  int n = 0;
+  float gs = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kWave) {
+    const int k = k0 + lane;
+    const bool in = k < K;
+    const int r = in ? slot_row[(size_t)t * K + k] : 0;
+    const float g = in ? gate[(size_t)t * K + k] : 0.0f;
+    const bool ffn = in && r >= 0;
+    const unsigned long long m = __ballot(ffn);
+    if (ffn) {
+      const int pos = n + __popcll(m & ((1ull << lane) - 1ull));
+      sl.rows[pos] = r;
+      sl.wts[pos] = scale * g;
+    }
+    n += __popcll(m);
+    for (unsigned long long b = __ballot(in && r < 0); b; b &= b - 1ull)
+      gs += __shfl(g, __ffsll((long long)b) - 1);
+  }
+  if (lane == 0) {
+    sl.n = n;
+    sl.identity_gate = gs;
+  }
+}
+
+// y[t] = ident[t] + sum over FFN slots (in slot order) of (scale*gate) * y_perm[row]
+//   IDENTITY = false: ident[t] = y_acc[t] (fp32, from zero_experts_kernel);
+//   IDENTITY = true:  ident[t] = (sum of the identity slots' gates) * x[t],
+//     computed here with the same fp32 operations, so the result is bitwise
+//     that of the two kernels, without y_acc's 4H bytes written and read
+//     per token.
+template <typename T, bool IDENTITY>
 __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
     const T* __restrict__ y_perm, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ gate, float scale, const float* __restrict__ y_acc, int H, int K,
-    T* __restrict__ y) {
-  __shared__ int rows[kMaxK];
-  __shared__ float wts[kMaxK];
-  __shared__ int nrows;
+    const float* __restrict__ gate, float scale, const float* __restrict__ y_acc,
+    const T* __restrict__ x, int H, int K, T* __restrict__ y) {
+  __shared__ SlotList sl;
   const int t = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int k = 0; k < K; ++k) {
-      int r = slot_row[(size_t)t * K + k];
-      if (r >= 0) {
-        rows[n] = r;
-        wts[n] = scale * gate[(size_t)t * K + k];
-        ++n;
-      }
-    }
-    nrows = n;
-  }
+  if (threadIdx.x < kWave) read_slots(sl, slot_row, gate, scale, K, t);
   __syncthreads();
-  const int n = nrows;
-  const float* ar = y_acc + (size_t)t * H;
+  const int n = sl.n;
+  const float gs = sl.identity_gate;
   T* yr = y + (size_t)t * H;
   for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
     float acc[8];
-    Vec8<float>::load(ar + c, acc);
+    if constexpr (IDENTITY) {
+      Vec8<T>::load(x + (size_t)t * H + c, acc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= gs;
+    } else {
+      Vec8<float>::load(y_acc + (size_t)t * H + c, acc);
+    }
     // up to kBatch rows in flight per thread; accumulation stays in slot order
     for (int j0 = 0; j0 < n; j0 += kBatch) {
       float v[kBatch][8];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (j0 + u < n) Vec8<T>::load(y_perm + (size_t)rows[j0 + u] * H + c, v[u]);
+        if (j0 + u < n) Vec8<T>::load(y_perm + (size_t)sl.rows[j0 + u] * H + c, v[u]);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (j0 + u >= n) break;
-        const float w = wts[j0 + u];
+        const float w = sl.wts[j0 + u];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
       }
@@ -137,16 +174,20 @@ hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, con
 }
 
 hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row,
-                          const float* gate, float scale, const float* y_acc, int T, int H,
-                          int K, void* y, hipStream_t s) {
-  if (dtype == MOE_BF16)
-    MOE_LAUNCH("combine", s,
-               combine_kernel<bf16><<<T, row_threads(H), 0, s>>>(
-                   (const bf16*)y_perm, slot_row, gate, scale, y_acc, H, K, (bf16*)y));
-  else
-    MOE_LAUNCH("combine", s,
-               combine_kernel<float><<<T, row_threads(H), 0, s>>>(
-                   (const float*)y_perm, slot_row, gate, scale, y_acc, H, K, (float*)y));
+                          const float* gate, float scale, const float* y_acc, const void* x,
+                          int T, int H, int K, void* y, hipStream_t s) {
+#define MOE_COMBINE(TY, ID)                                                                  \
+  combine_kernel<TY, ID><<<T, row_threads(H), 0, s>>>((const TY*)y_perm, slot_row, gate,     \
+                                                       scale, y_acc, (const TY*)x, H, K,     \
+                                                       (TY*)y)
+  if (dtype == MOE_BF16) {
+    if (x) MOE_LAUNCH("combine_identity", s, MOE_COMBINE(bf16, true));
+    else MOE_LAUNCH("combine", s, MOE_COMBINE(bf16, false));
+  } else {
+    if (x) MOE_LAUNCH("combine_identity", s, MOE_COMBINE(float, true));
+    else MOE_LAUNCH("combine", s, MOE_COMBINE(float, false));
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -154,8 +154,22 @@ moe_status moe_combine(const void* y_perm, int dtype, const int32_t* slot_row,
   if (!aligned(y_perm, 16) || !aligned(y_acc, 16) || !aligned(y, 16) || !aligned(slot_row, 4) ||
       !aligned(topk_gate, 4))
     return MOE_ERR_ALIGN;
-  return launched(launch_combine(y_perm, dtype, slot_row, topk_gate, ffn_scale, y_acc, T, H, K, y,
-                                 (hipStream_t)stream));
+  return launched(launch_combine(y_perm, dtype, slot_row, topk_gate, ffn_scale, y_acc, nullptr,
+                                 T, H, K, y, (hipStream_t)stream));
+}
+
+moe_status moe_combine_identity(const void* y_perm, const void* x, int dtype,
+                                const int32_t* slot_row, const float* topk_gate, float ffn_scale,
+                                int T, int H, int K, void* y, void* stream) {
+  if (!y_perm || !x || !slot_row || !topk_gate || !y) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || H % 8 || K < 1 || K > kMaxKCombine || !fits_i32((long long)T * K))
+    return MOE_ERR_SHAPE;
+  if (!aligned(y_perm, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(slot_row, 4) ||
+      !aligned(topk_gate, 4))
+    return MOE_ERR_ALIGN;
+  return launched(launch_combine(y_perm, dtype, slot_row, topk_gate, ffn_scale, nullptr, x, T, H,
+                                 K, y, (hipStream_t)stream));
 }
 
 moe_status moe_bias_update(const int32_t* counts, int T, int n_ffn, float target, float kp,

@@ -78,9 +78,11 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
                              hipStream_t s);
 hipError_t launch_zero_experts(const void* x, int dtype, const int32_t* idx, const float* gate,
                                int T, int H, int K, int n_ffn, float* y_acc, hipStream_t s);
+// x == nullptr: the identity term is y_acc; otherwise it is computed from x
+// and the identity slots' gates (slot_row < 0) and y_acc is not read.
 hipError_t launch_combine(const void* y_perm, int dtype, const int32_t* slot_row,
-                          const float* gate, float scale, const float* y_acc, int T, int H,
-                          int K, void* y, hipStream_t s);
+                          const float* gate, float scale, const float* y_acc, const void* x,
+                          int T, int H, int K, void* y, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, int T, int n_ffn, float target, float kp,
                               float ki, float kd, float* bias, float* integral, float* prev,
                               hipStream_t s);

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -149,6 +149,28 @@ def test_zero_and_combine_validation():
     c = moe.lib().moe_combine
     assert c(FAKE, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE, 8, 128, 2000, FAKE, None) == SHAPE
     assert c(FAKE, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE, 8, 128, 4, P(0x10004), None) == ALIGN
+
+
+def test_combine_identity_validation():
+    f = moe.lib().moe_combine_identity
+    one = ctypes.c_float(1.0)
+    args = [FAKE, FAKE, 1, FAKE, FAKE, one, 8, 128, 4, FAKE, None]
+    a = list(args); a[1] = None                   # x
+    assert f(*a) == NULL
+    a = list(args); a[3] = None                   # slot_row
+    assert f(*a) == NULL
+    a = list(args); a[2] = 3
+    assert f(*a) == DTYPE
+    a = list(args); a[7] = 100                    # H % 8
+    assert f(*a) == SHAPE
+    a = list(args); a[8] = 2000                   # K beyond the slot list
+    assert f(*a) == SHAPE
+    a = list(args); a[6] = 0
+    assert f(*a) == SHAPE
+    a = list(args); a[1] = P(0x10008)             # x rows not 16-byte aligned
+    assert f(*a) == ALIGN
+    a = list(args); a[9] = P(0x10004)             # y
+    assert f(*a) == ALIGN
 
 
 def test_binding_rejects_host_tensors():

@@ -101,12 +101,13 @@ def test_full_scale_layer(name, shared_weights):
         e3 = max(e3, err)
     assert e3 <= tol, e3
 
-    # S4: identity-expert rows of sampled tokens on the GPU's ids and gates
+    # S4: identity-expert term of sampled tokens on the GPU's ids and gates;
+    # combine computed it itself (the benchmarked path keeps no y_acc), so it
+    # is checked inside y below
+    assert buf["y_acc"] is None
     gate = host(buf["topk_gate"]).astype(np.float64)
     tsel = torch.from_numpy(toks).to(dev)
     yacc_ref = oracle.zero_experts(xs, idx[toks], gate[toks], N)
-    e4 = normwise(host(buf["y_acc"][tsel]), yacc_ref)
-    assert e4 <= 1e-6, e4
 
     # S5: combine of sampled tokens on the GPU's y_perm rows
     slots = slot_ref.reshape(cfg.T, K)[toks]
@@ -114,8 +115,7 @@ def test_full_scale_layer(name, shared_weights):
     remap = np.full(slots.shape, -1, np.int32)
     remap[slots >= 0] = np.arange(used.size)
     yp = host(buf["y_perm"][torch.from_numpy(used.astype(np.int64)).to(dev)]).astype(np.float64)
-    y_ref = oracle.combine(yp, remap.ravel(), idx[toks], gate[toks], cfg.scale,
-                           host(buf["y_acc"][tsel]).astype(np.float64), N)
+    y_ref = oracle.combine(yp, remap.ravel(), idx[toks], gate[toks], cfg.scale, yacc_ref, N)
     e5 = normwise(host(buf["y"][tsel]), y_ref)
     assert e5 <= tol, e5
 
@@ -145,7 +145,7 @@ def test_full_scale_layer(name, shared_weights):
         yacc = oracle.zero_experts(xe[n:n + 1], choice[None, :], g, N)
         y_e[n] = oracle.combine(outs, slot_map, choice[None, :], g, cfg.scale, yacc, N)[0]
     e_end = normwise(host(buf["y"][torch.from_numpy(ends).to(dev)]), y_e)
-    print(f"  {name}: logits {e0:.2e} gates {e1:.2e} y_perm {e3:.2e} y_acc {e4:.2e} "
+    print(f"  {name}: logits {e0:.2e} gates {e1:.2e} y_perm {e3:.2e} "
           f"y {e5:.2e} end-to-end {e_end:.2e} (flips {flips}); S={S}, "
           f"active experts {live.size}", flush=True)
     assert e_end <= tol, e_end

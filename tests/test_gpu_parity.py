@@ -14,14 +14,22 @@ from _parity import (TOL, check_end_to_end, device, forward, host, inputs_on_hos
 pytestmark = pytest.mark.gpu
 
 
-def _run(cfg, bias=None, grouped_copy=False):
+# Paths of forward(): "fast" = the default buffers (dispatch indices only, the
+# expert GEMM gathering rows from x, combine folding in the identity experts:
+# moe_expert_ffn_gather + moe_combine_identity); "stages" = every stage's
+# buffer kept (grouped copy x_perm, y_acc: moe_expert_ffn, moe_zero_experts,
+# moe_combine).
+PATHS = {"fast": {}, "stages": {"grouped_copy": True, "separate_identity": True}}
+
+
+def _run(cfg, bias=None, path="fast"):
     dev = device()
-    print(f"\n[case] {cfg} grouped_copy={grouped_copy}", flush=True)
+    print(f"\n[case] {cfg} path={path}", flush=True)
     inp = workload.make_inputs(cfg, dev)
     if bias is not None:
         inp["bias"] = torch.as_tensor(bias, dtype=torch.float32, device=dev)
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
-                            grouped_copy=grouped_copy)
+                            **PATHS[path])
     forward(cfg, inp, buf)
     return inp, buf
 
@@ -35,20 +43,18 @@ def _e2e(cfg, inp, buf, tokens=None):
     return err
 
 
-# grouped_copy: dispatch copies the rows (moe_permute + moe_expert_ffn);
-# otherwise the expert GEMM gathers them from x (moe_expert_ffn_gather).
-@pytest.mark.parametrize("grouped_copy", [False, True])
-def test_tiny_fp32_layer(grouped_copy):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_tiny_fp32_layer(path):
     cfg = workload.CONFIGS["tiny_fp32"]
-    inp, buf = _run(cfg, grouped_copy=grouped_copy)
+    inp, buf = _run(cfg, path=path)
     print(stage_checks(cfg, inp, buf))
     _e2e(cfg, inp, buf)
 
 
-@pytest.mark.parametrize("grouped_copy", [False, True])
-def test_mid_bf16_layer(grouped_copy):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_mid_bf16_layer(path):
     cfg = workload.CONFIGS["mid_bf16"]
-    inp, buf = _run(cfg, grouped_copy=grouped_copy)
+    inp, buf = _run(cfg, path=path)
     counts = host(buf["counts"])[:cfg.N]
     order = np.argsort(counts)
     experts = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
@@ -101,12 +107,13 @@ def test_largest_expert_pool(T):
     _e2e(cfg, inp, buf)
 
 
-def test_all_zero_expert_routing_returns_scaled_x():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_all_zero_expert_routing_returns_scaled_x(path):
     cfg = workload.MoEConfig("all_zero", T=130, H=256, N=6, Z=4, I=128, K=3, dtype="bf16",
                              sigma_w=0.05, bias_lo=0.0, bias_hi=0.0, scale=1.0)
     bias = np.zeros(cfg.E, np.float32)
     bias[cfg.N:] = 1e3
-    inp, buf = _run(cfg, bias)
+    inp, buf = _run(cfg, bias, path)
     assert (host(buf["topk_idx"]) >= cfg.N).all()
     assert int(host(buf["offsets"])[-1]) == 0
     assert (host(buf["slot_row"]) == -1).all()
@@ -116,14 +123,16 @@ def test_all_zero_expert_routing_returns_scaled_x():
     _e2e(cfg, inp, buf)
 
 
-def test_all_ffn_routing_has_no_identity_term():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_all_ffn_routing_has_no_identity_term(path):
     cfg = workload.MoEConfig("all_ffn", T=130, H=256, N=6, Z=4, I=128, K=3, dtype="bf16",
                              sigma_w=0.05, bias_lo=0.0, bias_hi=0.0, scale=2.0)
     bias = np.zeros(cfg.E, np.float32)
     bias[cfg.N:] = -1e3
-    inp, buf = _run(cfg, bias)
+    inp, buf = _run(cfg, bias, path)
     assert (host(buf["topk_idx"]) < cfg.N).all()
-    assert (host(buf["y_acc"]) == 0).all()
+    if buf["y_acc"] is not None:
+        assert (host(buf["y_acc"]) == 0).all()
     stage_checks(cfg, inp, buf)
     _e2e(cfg, inp, buf)
 
@@ -181,13 +190,14 @@ def test_forward_is_bitwise_deterministic():
     assert torch.equal(buf["y_perm"][:S], yp1[:S])
 
 
-@pytest.mark.parametrize("grouped_copy", [False, True])
-def test_rows_past_the_grouped_rows_are_untouched(grouped_copy):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_rows_past_the_grouped_rows_are_untouched(path):
     cfg = workload.CONFIGS["tiny_fp32"].replace(T=100)
     dev = device()
     inp = workload.make_inputs(cfg, dev)
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
-                            grouped_copy=grouped_copy)
+                            **PATHS[path])
+    grouped_copy = buf["x_perm"] is not None
     if grouped_copy:
         buf["x_perm"].fill_(123.0)
     buf["y_perm"].fill_(-7.0)
@@ -231,7 +241,8 @@ def test_two_stream_forward_matches_serial():
     assert cfg.T >= moe.OVERLAP_MIN_TOKENS
     dev = device()
     inps = [workload.make_inputs(cfg.replace(seed=s), dev) for s in (0, 1)]
-    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                            separate_identity=True)
 
     def run(fn, inp):
         buf["y_acc"].fill_(float("nan"))
@@ -306,3 +317,38 @@ def test_row_gather_clamps_out_of_range_sources(dtype):
     torch.cuda.synchronize()
     assert torch.equal(y_got[:S], y_ref[:S])
     assert (host(y_got[S:]) == 0).all()
+
+
+@pytest.mark.parametrize("name,T,zero_bias", [("tiny_fp32", None, 0.0), ("mid_bf16", 2048, 0.0),
+                                              ("mid_bf16", 65, 0.0), ("mid_bf16", 300, 50.0),
+                                              ("mid_bf16", 300, -50.0)])
+def test_combine_identity_matches_six_calls(name, T, zero_bias):
+    # moe_combine_identity computes the identity experts' term inside combine
+    # with the fp32 operations of moe_zero_experts + moe_combine, so y must
+    # be bitwise equal.  T = 2048 puts the six-call path on its two streams;
+    # a bias of +50 / -50 on the identity experts routes every pick to them /
+    # none of them (an empty / a full FFN slot list).
+    cfg = workload.CONFIGS[name]
+    if T is not None:
+        cfg = cfg.replace(T=T)
+    dev = device()
+    inp = workload.make_inputs(cfg, dev)
+    if zero_bias:
+        bias = np.zeros(cfg.E, np.float32)
+        bias[cfg.N:] = zero_bias
+        inp["bias"] = torch.as_tensor(bias, device=dev)
+    ys = {}
+    for sep in (False, True):
+        buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
+                                separate_identity=sep)
+        assert (buf["y_acc"] is None) == (not sep)
+        forward(cfg, inp, buf)
+        ys[sep] = buf["y"].clone()
+    S = int(host(buf["offsets"])[-1])
+    if zero_bias > 0:
+        assert S == 0
+    if zero_bias < 0:
+        assert S == cfg.T * cfg.K
+    assert torch.equal(ys[False], ys[True])
+    if zero_bias == 0.0 and name == "mid_bf16" and T == 65:
+        _e2e(cfg, inp, buf)
