@@ -219,6 +219,184 @@ __global__ __launch_bounds__(kRThreads, 1) void router_mfma(const bf16* __restri
   }
 }
 
+// ------------------------------------------------ wide tiles (prefill) --
+// Large batches: 256 tokens x 96 experts per block, K steps of 32.  The 128 x
+// 64 tiles above move 32 KB from L2 into LDS per 3.1 MFLOP step, and that
+// traffic, not the matrix cores, bounds them; a 256 x 96 tile moves 28 KB
+// per 4.7 MFLOP step (1.7x fewer bytes per flop), and at 768 experts the
+// 8192-token layer is exactly 256 blocks, one per CU.  A 64-element K step
+// would leave room for only two 56 KB stages, so the step is 32: x rows are
+// 64 B in LDS (4 chunks, swizzled by (row >> 1) & 3 so that any 8
+// consecutive rows' chunk c land in 8 distinct 16-byte bank groups) and
+// weight rows 128 B (8 chunks, swizzled by row & 7).  Compute wave (wr, wc)
+// owns tokens [128 wr, +128) x experts [48 wc, +48): 8 x 3 16 x 16 blocks,
+// and splits its 3 weight column blocks into the three bf16 planes per step.
+// The loaders issue the weight halves of the fill before the x halves (the
+// weights come from the last-level cache or HBM; x from L2), as the expert
+// GEMM does.  Every compute and loader wave helps write the output tile.
+constexpr int kWM = 256, kWN = 96, kWK = 32;
+constexpr int kWAStage = kWM * kWK * 2;           // 16 KB of x
+constexpr int kWBStage = kWN * kWK * 4;           // 12 KB of fp32 weights
+constexpr int kWStageBytes = kWAStage + kWBStage;
+constexpr int kWS = 5;                            // ring stages (140 KB)
+constexpr int kWQa = kWAStage / 1024 / 4;         // x loads per loader per step (4)
+constexpr int kWQb = kWBStage / 1024 / 4;         // weight loads per loader per step (3)
+constexpr int kWQ = kWQa + kWQb;
+constexpr int kWPitch = kWN * 4 + 16;             // output tile row pitch (bytes)
+static_assert(kWM * kWPitch <= kWS * kWStageBytes, "output tile fits the ring");
+static_assert((kWS - 2) * kWQ < 64, "vmcnt range");
+
+__device__ __forceinline__ int swz4(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+
+// Ring steps 0..kWS-2 after the split fill: step kt's x loads have the fill's
+// later x loads and kt whole steps behind them.
+template <int KT0, class F>
+__device__ __forceinline__ void wide_head(int KT, F& issue) {
+  if constexpr (KT0 < kWS - 1) {
+    if (KT0 >= KT) return;
+    wait_vmcnt<(kWS - 2 - KT0) * kWQa + KT0 * kWQ>();
+    lds_barrier();
+    issue(KT0 + kWS - 1);
+    wide_head<KT0 + 1>(KT, issue);
+  }
+}
+
+__global__ __launch_bounds__(kRThreads, 1) void router_wide(const bf16* __restrict__ x,
+                                                            const float* __restrict__ w, int T,
+                                                            int H, int E, int NTE,
+                                                            float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) char smem[kWS * kWStageBytes];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NTE) * 8 + xcd;   // the expert tiles of a token tile share an XCD
+  const int nt = slot % NTE;
+  const int m0 = mt * kWM, n0 = nt * kWN;
+  if (m0 >= T) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KT = H / kWK;
+  const int k_start = ((nt & 1) * KT) / 2;   // two K offsets by tile parity
+
+  if (wave >= 4) {
+    const int l = wave - 4;
+    const bf16* a_src[kWQa];
+    const float* b_src[kWQb];
+    // instruction q of loader l covers x rows 16 (l + 4q) .. +16 (4 lanes a
+    // row) and weight rows 8 (l + 4q) .. +8 (8 lanes a row); lane j's 16
+    // bytes land at byte 16 j of the instruction's 1 KB.
+#pragma unroll
+    for (int q = 0; q < kWQa; ++q) {
+      const int ra = (l + 4 * q) * 16 + (lane >> 2);
+      a_src[q] = x + (size_t)min(m0 + ra, T - 1) * H + swz4(ra, lane & 3) * 8;
+    }
+#pragma unroll
+    for (int q = 0; q < kWQb; ++q) {
+      const int rb = (l + 4 * q) * 8 + (lane >> 3);
+      b_src[q] = w + (size_t)min(n0 + rb, E - 1) * H + swz8(rb, lane & 7) * 4;
+    }
+    auto k_of = [&](int kt) {
+      int ks = kt + k_start;
+      ks = ks >= KT ? ks - KT : ks;
+      return kt < KT ? ks * kWK : 0;
+    };
+    auto issue_a = [&](int kt) {
+      char* sb = smem + (kt % kWS) * kWStageBytes;
+      const int k0 = k_of(kt);
+#pragma unroll
+      for (int q = 0; q < kWQa; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + k0),
+                                         (lds_void*)(sb + (l + 4 * q) * 1024), 16, 0, 0);
+    };
+    auto issue_b = [&](int kt) {
+      char* sb = smem + (kt % kWS) * kWStageBytes;
+      const int k0 = k_of(kt);
+#pragma unroll
+      for (int q = 0; q < kWQb; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[q] + k0),
+                                         (lds_void*)(sb + kWAStage + (l + 4 * q) * 1024), 16, 0,
+                                         0);
+    };
+    auto issue = [&](int kt) {
+      issue_a(kt);
+      issue_b(kt);
+    };
+    for (int kt = 0; kt < kWS - 1; ++kt) issue_b(kt);
+    for (int kt = 0; kt < kWS - 1; ++kt) issue_a(kt);
+    wide_head<0>(KT, issue);
+    for (int kt = kWS - 1; kt < KT; ++kt) {
+      wait_vmcnt<(kWS - 2) * kWQ>();   // step kt has landed (in-order completion)
+      lds_barrier();                   // publish it; every wave is done with step kt - 1
+      issue(kt + kWS - 1);             // into the stage step kt - 1 used
+    }
+    wait_vmcnt<0>();
+    lds_barrier();   // the LDS is free for the output tile
+  } else {
+    const int wr = wave >> 1, wc = wave & 1;
+    f32x4 acc[8][3];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+    for (int kt = 0; kt < KT; ++kt) {
+      lds_barrier();
+      const char* As = smem + (kt % kWS) * kWStageBytes;
+      const char* Bs = As + kWAStage;
+      // lane l: k elements 8 (l >> 4) .. + 8 of the step = x chunk l >> 4,
+      // fp32 weight chunks 2 (l >> 4) and 2 (l >> 4) + 1
+      const int c = lane >> 4;
+      bf16x8 bh[3], bm[3], bl[3];
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) {
+        const int rB = 48 * wc + 16 * cb + (lane & 15);
+        const f32x4 v0 = *(const f32x4*)(Bs + rB * 128 + swz8(rB, 2 * c) * 16);
+        const f32x4 v1 = *(const f32x4*)(Bs + rB * 128 + swz8(rB, 2 * c + 1) * 16);
+        split3(v0, v1, bh[cb], bm[cb], bl[cb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb) {
+        const int rA = 128 * wr + 16 * rb + (lane & 15);
+        const bf16x8 a = *(const bf16x8*)(As + rA * 64 + swz4(rA, c) * 16);
+#pragma unroll
+        for (int cb = 0; cb < 3; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[cb], acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();   // loads landed, fragments read: the LDS is free
+    // acc[rb][cb] element i: token 128 wr + 16 rb + 4 (l >> 4) + i,
+    // expert 48 wc + 16 cb + (l & 15)
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 128 * wr + 16 * rb + 4 * (lane >> 4) + i;
+          *(float*)(smem + r * kWPitch + (48 * wc + 16 * cb + (lane & 15)) * 4) = acc[rb][cb][i];
+        }
+  }
+  lds_barrier();   // the output tile is complete
+  // all 8 waves store it, 16 bytes per lane, whole 16-byte pieces when the
+  // tile is in range and aligned
+  const bool full = n0 + kWN <= E && (E & 3) == 0 && ((uintptr_t)logits & 15) == 0;
+  constexpr int kQuads = kWN / 4;
+  for (int j = threadIdx.x; j < kWM * kQuads; j += kRThreads) {
+    const int r = j / kQuads, cq = j - r * kQuads;
+    if (m0 + r >= T) continue;
+    const f32x4 v = *(const f32x4*)(smem + r * kWPitch + cq * 16);
+    float* dst = logits + (size_t)(m0 + r) * E + n0 + 4 * cq;
+    if (full) {
+      *(f32x4*)dst = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n0 + 4 * cq + u < E) dst[u] = v[u];
+    }
+  }
+}
+
 // ------------------------------------------------- few tokens (decode) --
 // With T <= 64 the 128 x 64 tiles above leave a dozen blocks for the whole
 // chip, each streaming 64 experts' weights over all of H.  Here a block takes
@@ -300,6 +478,15 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
     MOE_LAUNCH("router_logits", s,
                router_small<<<ceil_div(E, kSmallN), kSmallWaves * kWave, 0, s>>>(
                    (const bf16*)x, w, T, H, E, logits));
+    return hipGetLastError();
+  }
+  if (dtype == MOE_BF16 && H % kWK == 0 &&
+      (long long)ceil_div(T, kWM) * ceil_div(E, kWN) >= 256) {   // enough wide tiles for every CU
+    const int nte = (E + kWN - 1) / kWN;
+    const unsigned groups = ceil_div(ceil_div(T, kWM), 8);
+    MOE_LAUNCH("router_logits", s,
+               router_wide<<<groups * 8 * nte, kRThreads, 0, s>>>((const bf16*)x, w, T, H, E,
+                                                                  nte, logits));
     return hipGetLastError();
   }
   if (dtype == MOE_BF16 && H % kRK == 0) {
