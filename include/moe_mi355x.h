@@ -220,9 +220,13 @@ moe_status moe_router_similarity(const float *w_router, int E, int H, float *sim
  * state.  moe_profile_summary waits for the recorded events and writes one
  * line "kernel_name launches total_ms" per kernel into buf (at most len
  * bytes, NUL-terminated); it returns the length of the full text, or -1 if an
- * event could not be read.  The session is process-wide; concurrent callers
- * share it. */
+ * event could not be read.  moe_profile_select restricts the timing to the
+ * kernels named in a comma-separated list (NULL or "": every kernel) and
+ * returns the number of names; each bracketed launch costs a few
+ * microseconds of stream time, so timed loops select what they need.  The
+ * session is process-wide; concurrent callers share it. */
 int moe_profile_enable(int on);
+int moe_profile_select(const char *names);
 int moe_profile_summary(char *buf, size_t len);
 
 /* Human-readable name of a status code (static storage). */

@@ -46,6 +46,7 @@ _SIGS = {
     "moe_router_similarity": ([_P, _I, _I, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_profile_enable": ([_I], _I),
+    "moe_profile_select": ([ctypes.c_char_p], _I),
     "moe_profile_summary": ([ctypes.c_char_p, ctypes.c_size_t], _I),
 }
 
@@ -263,6 +264,12 @@ def moe_router_similarity(w_router, sim, mean, ws):
 def moe_profile_enable(on: bool) -> bool:
     """Start (True) or stop (False) per-kernel event timing; returns the old state."""
     return bool(lib().moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_select(names=None) -> int:
+    """Time only the named kernels (an iterable of names; None: every kernel)."""
+    arg = None if names is None else ",".join(names).encode()
+    return int(lib().moe_profile_select(arg))
 
 
 def moe_profile_summary() -> dict:

@@ -1,8 +1,11 @@
 // Opt-in per-kernel timing with HIP events (a diagnostic, off by default).
-// While enabled, every kernel the library enqueues is bracketed by two events
-// recorded on the same stream; the summary waits for them and reports, per
-// kernel name, the number of launches and the summed elapsed time.  When
-// disabled the cost is one relaxed atomic load per launch.
+// While enabled, every kernel the library enqueues -- or only the kernels
+// named by moe_profile_select -- is bracketed by two events recorded on the
+// same stream; the summary waits for them and reports, per kernel name, the
+// number of launches and the summed elapsed time.  Each bracketed launch
+// costs a few microseconds of stream time, so a timed loop should select
+// only the kernels it needs.  When disabled the cost is one relaxed atomic
+// load per launch.
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -25,6 +28,14 @@ std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Rec> g_recs;            // this profiling session
 std::vector<hipEvent_t> g_pool;     // events kept for reuse across sessions
+std::vector<std::string> g_sel;     // kernels to time; empty: every kernel
+
+bool selected_locked(const char* name) {
+  if (g_sel.empty()) return true;
+  for (const auto& s : g_sel)
+    if (s == name) return true;
+  return false;
+}
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -50,9 +61,13 @@ void recycle_locked() {
 int prof_begin(const char* name, hipStream_t s) {
   if (!g_on.load(std::memory_order_relaxed)) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!selected_locked(name)) return -1;
   Rec r{name, take_event(), take_event()};
-  if (!r.a || !r.b) return -1;
-  hipEventRecord(r.a, s);
+  if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+    return -1;
+  }
   g_recs.push_back(r);
   return (int)g_recs.size() - 1;
 }
@@ -60,7 +75,9 @@ int prof_begin(const char* name, hipStream_t s) {
 void prof_end(int token, hipStream_t s) {
   if (token < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (token < (int)g_recs.size()) hipEventRecord(g_recs[token].b, s);
+  // a failed record leaves the end event unrecorded: the summary then
+  // reports the failure instead of a time
+  if (token < (int)g_recs.size()) (void)hipEventRecord(g_recs[token].b, s);
 }
 
 }  // namespace moe
@@ -76,6 +93,28 @@ int moe_profile_enable(int on) {
   if (on) recycle_locked();
   g_on.store(on != 0);
   return was ? 1 : 0;
+}
+
+/* Time only the kernels named in `names`, a comma-separated list (e.g.
+ * "ffn_gateup_bf16,ffn_down_bf16"); NULL or "" times every kernel.  Applies
+ * from the next launch.  Returns the number of names selected. */
+int moe_profile_select(const char* names) {
+  using namespace moe;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_sel.clear();
+  if (names) {
+    std::string cur;
+    for (const char* p = names;; ++p) {
+      if (*p == ',' || *p == 0) {
+        if (!cur.empty()) g_sel.push_back(cur);
+        cur.clear();
+        if (*p == 0) break;
+      } else if (*p != ' ') {
+        cur += *p;
+      }
+    }
+  }
+  return (int)g_sel.size();
 }
 
 /* Waits for the recorded events and writes one line per kernel name,
