@@ -45,7 +45,10 @@ constexpr int kThreads = 256;        // fp32 path and the small kernels
 constexpr int kGemmThreads = 512;    // bf16 GEMM: 4 compute + 4 loader waves
 constexpr int kBK = 64;                 // k elements per pipeline step
 constexpr int kRowBytes = kBK * 2;      // 128 B per LDS row of a step
-constexpr int kBN = 128;                // weight rows per block
+constexpr int kBN = 128;                // weight rows per block (down, partial tiles: 192)
+constexpr int kBNWide = 192;
+constexpr int kAllGroups = 0x1FE;       // bits 1..8: m-tiles of 1-8 32-row groups
+constexpr int kWideGroups = 0x0FC;      // bits 2..7: the down GEMM's 192-row tiles
 constexpr int kBmBf16 = 256;
 constexpr int kBmF32 = 32;
 
@@ -110,12 +113,12 @@ constexpr int kLdsBytes = 160 * 1024;
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kCachePolicyNT = 2;   // non-temporal: weights are streamed once
 
-template <int G>
+template <int G, int BN = kBN>
 struct Ring {
   static constexpr int kABytes = 32 * G * kRowBytes;   // A tile of one step
-  static constexpr int kStageBytes = kABytes + kBN * kRowBytes;
+  static constexpr int kStageBytes = kABytes + BN * kRowBytes;
   static constexpr int kQa = G;                        // A loads per loader per step
-  static constexpr int kQb = kBN / 8 / 4;              // B loads per loader per step (4)
+  static constexpr int kQb = BN / 8 / 4;               // B loads per loader per step (4 or 6)
   static constexpr int kQ = kQa + kQb;
   static constexpr int kFit = kLdsBytes / kStageBytes;
   static constexpr int S = kFit > 8 ? 8 : kFit;
@@ -135,15 +138,16 @@ struct TileSrc {
   int a_step;           // elements between K steps of one row block
 };
 
-// Weight row held in row r (0..127) of the block's weight tile.  Gate/up:
-// rows 32w + [0,16) are gate rows j, 32w + [16,32) the up rows of the same j,
-// so that one lane ends up with gate column j and up column j.
+// Weight row held in row r (0..BN-1) of the block's weight tile.  Gate/up
+// (BN = 128): rows 32w + [0,16) are gate rows j, 32w + [16,32) the up rows of
+// the same j, so that one lane ends up with gate column j and up column j.
+template <int BN>
 __device__ __forceinline__ int weight_row(const TileSrc& t, int r) {
   if (t.gateup) {
     const int j = t.nt * 64 + 16 * (r >> 5) + (r & 15);
     return (r & 16) ? t.I + j : j;
   }
-  return t.nt * kBN + r;
+  return t.nt * BN + r;
 }
 
 // Steps 0..S-2 of the loader's sweep, after the split fill: step kt's
@@ -167,10 +171,10 @@ __device__ __forceinline__ void ring_head(int KT, F& issue) {
 // same loads -- past the end they read one fixed line into a stage no one
 // reads again -- so every wait count is a constant.  The sweep starts at
 // k_start and wraps around.
-template <int G, bool GATHER>
+template <int G, bool GATHER, int BN>
 __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD, int k_start,
                                            int l, int lane) {
-  using R = Ring<G>;
+  using R = Ring<G, BN>;
   constexpr int S = R::S, kQ = R::kQ;
   const int KT = KD / kBK;
   const int lr = lane >> 3, lc = lane & 7;
@@ -204,7 +208,7 @@ __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD,
 #pragma unroll
   for (int i = 0; i < R::kQb; ++i) {
     const int r = (l + 4 * i) * 8 + lr;
-    src[R::kQa + i] = t.w + (size_t)weight_row(t, r) * KD + swz(r, lc) * 8;
+    src[R::kQa + i] = t.w + (size_t)weight_row<BN>(t, r) * KD + swz(r, lc) * 8;
   }
   auto stage = [&](int kt) { return smem + (kt % S) * R::kStageBytes; };
   auto k_of = [&](int kt) { const int ks = kt + k_start; return ks >= KT ? ks - KT : ks; };
@@ -259,9 +263,9 @@ __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD,
 }
 
 // The compute waves' K sweep: step kt reads stage kt % S.
-template <int G, class Compute>
+template <int G, int BN, class Compute>
 __device__ __forceinline__ void ffn_consumer(char* smem, int KD, Compute&& compute) {
-  using R = Ring<G>;
+  using R = Ring<G, BN>;
   const int KT = KD / kBK;
   for (int kt = 0; kt < KT; ++kt) {
     lds_barrier();
@@ -270,20 +274,22 @@ __device__ __forceinline__ void ffn_consumer(char* smem, int KD, Compute&& compu
   }
 }
 
-// Partial tiles: wave w owns weight rows [32w, 32w+32) (two 16-column MFMA
-// blocks) and all 32G live rows.
-template <int G>
+// Partial tiles: wave w owns weight rows [16 CB w, +16 CB) (CB 16-column MFMA
+// blocks: 2 of a 128-row tile, 3 of a 192-row one) and all 32G live rows.
+template <int G, int CB>
 struct ColumnSplit {
-  f32x4 (&acc)[kBmBf16 / 16][2];
+  f32x4 (&acc)[kBmBf16 / 16][CB];
   int wave, lane;
   __device__ __forceinline__ void operator()(const char* As, const char* Bs) const {
-    const int rB0 = 32 * wave + (lane & 15);
-    const int rB1 = rB0 + 16;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
-      const bf16x8 b0 = *(const bf16x8*)(Bs + rB0 * kRowBytes + swz(rB0, ch) * 16);
-      const bf16x8 b1 = *(const bf16x8*)(Bs + rB1 * kRowBytes + swz(rB1, ch) * 16);
+      bf16x8 b[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int rB = 16 * CB * wave + 16 * cb + (lane & 15);
+        b[cb] = *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, ch) * 16);
+      }
       bf16x8 a[2 * G];
 #pragma unroll
       for (int rb = 0; rb < 2 * G; ++rb) {
@@ -291,10 +297,10 @@ struct ColumnSplit {
         a[rb] = *(const bf16x8*)(As + rA * kRowBytes + swz(rA, ch) * 16);
       }
 #pragma unroll
-      for (int rb = 0; rb < 2 * G; ++rb) {
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b0, acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b1, acc[rb][1], 0, 0, 0);
-      }
+      for (int rb = 0; rb < 2 * G; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
     }
   }
 };
@@ -360,16 +366,27 @@ struct OutTile {
   }
 };
 static_assert(kBmBf16 * OutTile<kBN>::kPitch <= kLdsBytes, "output tile fits LDS");
+static_assert(224 * OutTile<kBNWide>::kPitch <= kLdsBytes, "partial output tile fits LDS");
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-template <bool GATEUP>
+// A ring of at least three stages fits LDS for G groups of 32 rows and BN
+// weight rows (192-row tiles: up to 7 groups).
+constexpr bool ring_fits(int G, int BN) {
+  return kLdsBytes / (32 * G * kRowBytes + BN * kRowBytes) >= 3;
+}
+
+// One launch covers the m-tiles whose number of 32-row groups g has bit g
+// set in gmask; the others' blocks exit at once.
+template <bool GATEUP, int BN>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
     const bf16* __restrict__ W, const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-    int KD, int I, int H, int NT, bf16* __restrict__ C) {
+    int KD, int I, int H, int NT, int gmask, bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
   static_assert(BM == 256, "instances cover 8 groups of 32 rows");
+  static_assert(!GATEUP || BN == kBN, "gate/up pairs gate and up rows in 128-row tiles");
+  constexpr int CB = BN / 64;   // 16-column MFMA blocks per compute wave (partial tiles)
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int b = blockIdx.x;
@@ -379,6 +396,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   if (mt >= *ntiles) return;
   const int4 tile = tiles[mt];
   const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const int groups = (rows + 31) >> 5;
+  if (!((gmask >> groups) & 1)) return;   // another launch's tile
+  if (!ring_fits(groups, BN)) return;     // never launched for (8 groups at BN 192)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
 
@@ -407,15 +427,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   const int n_start = rows == kBmBf16 ? 4 : rows <= 32 ? NT : (GATEUP ? 2 : 1);
   const int k_start = ((nt % n_start) * KT) / n_start;
 
-  const int groups = (rows + 31) >> 5;
   if (wave >= 4) {   // loader waves
     switch (groups) {
 #define MOE_CASE(g) \
       case g:                                                                  \
-        if (GATEUP && src.gather)                                              \
-          ffn_loader<g, GATEUP>(smem, src, KD, k_start, wave - 4, lane);       \
-        else                                                                   \
-          ffn_loader<g, false>(smem, src, KD, k_start, wave - 4, lane);        \
+        if constexpr (ring_fits(g, BN)) {                                      \
+          if (GATEUP && src.gather)                                            \
+            ffn_loader<g, GATEUP, BN>(smem, src, KD, k_start, wave - 4, lane); \
+          else                                                                 \
+            ffn_loader<g, false, BN>(smem, src, KD, k_start, wave - 4, lane);  \
+        }                                                                      \
         break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
       MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
@@ -429,17 +450,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     return;
   }
 
-  // Output tile: gate/up 64 hh columns, down 128 y columns of this column tile.
-  constexpr int NC = GATEUP ? kBN / 2 : kBN;
+  // Output tile: gate/up 64 hh columns, down BN y columns of this column tile.
+  constexpr int NC = GATEUP ? BN / 2 : BN;
   const OutTile<NC> out{smem};
   const int c = lane & 15, q = lane >> 4;
-  if (rows == BM) {
+  if (BN == kBN && rows == BM) {
     f32x4 acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-    ffn_consumer<8>(smem, KD, Quadrant{acc, wave, lane});
+    ffn_consumer<8, kBN>(smem, KD, Quadrant{acc, wave, lane});
     lds_barrier();   // loads landed, fragments read: the LDS is free
     // lane holds C[128 wr + 16 rb + 4 q + i][weight row 64 wc + 16 cb + c]
     const int wr = wave >> 1, wc = wave & 1;
@@ -459,35 +480,37 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
         }
       }
   } else {
-    f32x4 acc[BM / 16][2];
+    f32x4 acc[BM / 16][CB];
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
-      acc[i][0] = f32x4{0, 0, 0, 0};
-      acc[i][1] = f32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < BM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     // K loop instantiated per number of live 32-row groups: branch-free, only
     // the live rows are loaded and only their MFMAs issued.
     switch (groups) {
-#define MOE_CASE(g)                                                      \
-      case g: ffn_consumer<g>(smem, KD, ColumnSplit<g>{acc, wave, lane}); break;
+#define MOE_CASE(g)                                                                 \
+      case g:                                                                       \
+        if constexpr (ring_fits(g, BN))                                             \
+          ffn_consumer<g, BN>(smem, KD, ColumnSplit<g, CB>{acc, wave, lane});       \
+        break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
       MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
       default: break;
     }
     lds_barrier();   // loads landed, fragments read: the LDS is free
-    // lane holds C[16 rb + 4 q + i][weight row 32 wave + 16 cb + c]
+    // lane holds C[16 rb + 4 q + i][weight row 16 CB wave + 16 cb + c]
 #pragma unroll
     for (int rb = 0; rb < BM / 16; ++rb) {
       if (rb * 16 >= rows) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rb * 16 + 4 * q + i;
-        if (GATEUP) {
+        if constexpr (GATEUP) {
           out.put(r, 16 * wave + c, silu_mul(acc[rb][0][i], acc[rb][1][i]));
         } else {
-          out.put(r, 32 * wave + c, acc[rb][0][i]);
-          out.put(r, 32 * wave + 16 + c, acc[rb][1][i]);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) out.put(r, 16 * CB * wave + 16 * cb + c, acc[rb][cb][i]);
         }
       }
     }
@@ -594,13 +617,38 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
     MOE_LAUNCH("ffn_gateup_bf16", s,
-               ffn_mfma_bf16<true><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
+               ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
                    (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
-                   H, nt1, (bf16*)hh));
-    MOE_LAUNCH("ffn_down_bf16", s,
-               ffn_mfma_bf16<false><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
-                   (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
-                   nt2, (bf16*)y_perm));
+                   H, nt1, kAllGroups, (bf16*)hh));
+    // Down: m-tiles of 2-7 groups (33-224 rows) take 192-row weight tiles
+    // when H allows: a third less activation traffic from L2 per weight byte.
+    // Tiles of one group (pure weight streaming) keep the deeper ring of
+    // 128-row tiles (8 stages against 5), and 8-group tiles do not fit a
+    // 192-row ring, so these take a second launch.  The split pays where
+    // the typical expert has one partial tile -- 32 to 256 rows per FFN
+    // expert even if every pick went to one, decided from the capacity
+    // (measured on the 8192-token layer: 2.86 -> 2.53 ms).  With fewer rows
+    // (decode: every tile one group) the second launch is pure overhead
+    // (~16 us), and with more (heavy experts' full tiles next to light ones)
+    // two serial launches lose the single launch's interleaving (+0.14 ms on
+    // the 16384-token skewed layer).  One timing bracket covers both.
+    const bool wide = H % kBNWide == 0 && (long long)rows_cap >= 32LL * n_ffn &&
+                      (long long)rows_cap <= 256LL * n_ffn;
+    if (wide) {
+      const int ntw = H / kBNWide;
+      MOE_LAUNCH("ffn_down_bf16", s,
+                 ffn_mfma_bf16<false, kBNWide><<<groups * 8 * ntw, kGemmThreads, 0, s>>>(
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
+                     ntw, kWideGroups, (bf16*)y_perm);
+                 ffn_mfma_bf16<false, kBN><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
+                     nt2, kAllGroups & ~kWideGroups, (bf16*)y_perm));
+    } else {
+      MOE_LAUNCH("ffn_down_bf16", s,
+                 ffn_mfma_bf16<false, kBN><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
+                     nt2, kAllGroups, (bf16*)y_perm));
+    }
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
     MOE_LAUNCH("ffn_gateup_f32", s,
