@@ -8,11 +8,14 @@
 // (rows_cap / BM + n_ffn m-tiles) and blocks past the real count exit.
 //
 // bf16 path (gfx950 matrix cores, v_mfma_f32_16x16x32_bf16, fp32 accumulate):
-//   - one block = one m-tile (all of the expert's rows, up to BM) x 128 rows
+//   - one block = one m-tile (all of the expert's rows, up to BM) x BN rows
 //     of the weight matrix, so every weight tile is fetched from HBM once when
 //     an expert's rows fit one m-tile -- the regime of the full-scale layer,
-//     where the weights (not the MFMA rate) bound the time;
-//   - wave w owns 32 weight rows (two 16-column MFMA blocks) and every row
+//     where the weights (not the MFMA rate) bound the time.  BN = 128, or,
+//     for the partial tiles of a layer whose experts typically fit one tile,
+//     256 (gate/up) and 192 (down): the activation rows every column tile
+//     re-reads from L2 then cost less per weight byte (see launch_expert_ffn);
+//   - wave w owns BN / 4 weight rows (16-column MFMA blocks) and every row
 //     block of the m-tile; 32-row groups past the expert's rows are skipped;
 //   - 8 waves: four compute waves (fragment reads + MFMA only) and four
 //     loader waves that stream 64-element K steps by global->LDS DMA into a
@@ -49,6 +52,8 @@ constexpr int kBN = 128;                // weight rows per block (down, partial 
 constexpr int kBNWide = 192;
 constexpr int kAllGroups = 0x1FE;       // bits 1..8: m-tiles of 1-8 32-row groups
 constexpr int kWideGroups = 0x0FC;      // bits 2..7: the down GEMM's 192-row tiles
+constexpr int kBNGateUpWide = 256;      // gate/up: 128 hh columns per tile
+constexpr int kWideGroupsGateUp = 0x03C;   // bits 2..5: 256-row tiles (a 3-stage ring fits)
 constexpr int kBmBf16 = 256;
 constexpr int kBmF32 = 32;
 
@@ -138,13 +143,14 @@ struct TileSrc {
   int a_step;           // elements between K steps of one row block
 };
 
-// Weight row held in row r (0..BN-1) of the block's weight tile.  Gate/up
-// (BN = 128): rows 32w + [0,16) are gate rows j, 32w + [16,32) the up rows of
-// the same j, so that one lane ends up with gate column j and up column j.
+// Weight row held in row r (0..BN-1) of the block's weight tile.  Gate/up:
+// rows 32p + [0,16) are gate rows j, 32p + [16,32) the up rows of the same j
+// (BN / 2 hh columns per tile), so that one lane ends up with gate column j
+// and up column j.
 template <int BN>
 __device__ __forceinline__ int weight_row(const TileSrc& t, int r) {
   if (t.gateup) {
-    const int j = t.nt * 64 + 16 * (r >> 5) + (r & 15);
+    const int j = t.nt * (BN / 2) + 16 * (r >> 5) + (r & 15);
     return (r & 16) ? t.I + j : j;
   }
   return t.nt * BN + r;
@@ -364,6 +370,18 @@ struct OutTile {
       __builtin_nontemporal_store(v, (i32x4*)(dst + r * pitch + c * 8));
     }
   }
+  // hh, m-tile-blocked: column block b (64 columns) of the m-tile's rows sits
+  // contiguously at dst + b * rows * 64; this tile holds blocks b0 ..
+  // b0 + NC / 64 - 1.
+  __device__ __forceinline__ void flush_blocked(bf16* __restrict__ dst, int b0, int rows,
+                                                int tid) const {
+    for (int j = tid; j < rows * kChunks; j += 256) {
+      const int r = j / kChunks, c = j - r * kChunks;
+      const i32x4 v = *(const i32x4*)(t + r * kPitch + c * 16);
+      bf16* blk = dst + (size_t)(b0 + (c >> 3)) * rows * 64;
+      __builtin_nontemporal_store(v, (i32x4*)(blk + r * 64 + (c & 7) * 8));
+    }
+  }
 };
 static_assert(kBmBf16 * OutTile<kBN>::kPitch <= kLdsBytes, "output tile fits LDS");
 static_assert(224 * OutTile<kBNWide>::kPitch <= kLdsBytes, "partial output tile fits LDS");
@@ -385,7 +403,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     int KD, int I, int H, int NT, int gmask, bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
   static_assert(BM == 256, "instances cover 8 groups of 32 rows");
-  static_assert(!GATEUP || BN == kBN, "gate/up pairs gate and up rows in 128-row tiles");
   constexpr int CB = BN / 64;   // 16-column MFMA blocks per compute wave (partial tiles)
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
@@ -507,7 +524,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
       for (int i = 0; i < 4; ++i) {
         const int r = rb * 16 + 4 * q + i;
         if constexpr (GATEUP) {
-          out.put(r, 16 * wave + c, silu_mul(acc[rb][0][i], acc[rb][1][i]));
+          // column blocks 2p (gate) and 2p + 1 (up) of hh columns 16 (CB/2) wave + 16 p + c
+#pragma unroll
+          for (int p = 0; p < CB / 2; ++p)
+            out.put(r, 16 * (CB / 2) * wave + 16 * p + c,
+                    silu_mul(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]));
         } else {
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) out.put(r, 16 * CB * wave + 16 * cb + c, acc[rb][cb][i]);
@@ -516,8 +537,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     }
   }
   lds_barrier();   // the four compute waves' values are in the tile
-  if (GATEUP)   // hh, m-tile-blocked: this tile's rows x 64 columns, contiguous
-    out.flush(C + (size_t)row0 * I + (size_t)nt * rows * NC, NC, rows, threadIdx.x);
+  if (GATEUP)   // hh, m-tile-blocked in 64-column blocks (one down K step each)
+    out.flush_blocked(C + (size_t)row0 * I, nt * (NC / 64), rows, threadIdx.x);
   else          // y_perm, row-major
     out.flush(C + (size_t)row0 * H + nt * NC, H, rows, threadIdx.x);
 }
@@ -616,25 +637,39 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
   if (dtype == MOE_BF16) {
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
-    MOE_LAUNCH("ffn_gateup_bf16", s,
-               ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
-                   (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
-                   H, nt1, kAllGroups, (bf16*)hh));
-    // Down: m-tiles of 2-7 groups (33-224 rows) take 192-row weight tiles
-    // when H allows: a third less activation traffic from L2 per weight byte.
-    // Tiles of one group (pure weight streaming) keep the deeper ring of
-    // 128-row tiles (8 stages against 5), and 8-group tiles do not fit a
-    // 192-row ring, so these take a second launch.  The split pays where
-    // the typical expert has one partial tile -- 32 to 256 rows per FFN
-    // expert even if every pick went to one, decided from the capacity
-    // (measured on the 8192-token layer: 2.86 -> 2.53 ms).  With fewer rows
-    // (decode: every tile one group) the second launch is pure overhead
-    // (~16 us), and with more (heavy experts' full tiles next to light ones)
-    // two serial launches lose the single launch's interleaving (+0.14 ms on
-    // the 16384-token skewed layer).  One timing bracket covers both.
-    const bool wide = H % kBNWide == 0 && (long long)rows_cap >= 32LL * n_ffn &&
-                      (long long)rows_cap <= 256LL * n_ffn;
-    if (wide) {
+    // Where the typical expert has one partial m-tile -- 32 to 256 rows per
+    // FFN expert even if every pick went to one, decided from the capacity
+    // -- both GEMMs take wider weight tiles for their partial tiles, which
+    // cut the activation traffic from L2 per weight byte:
+    //   gate/up: 256 rows (128 hh columns) for tiles of 2-5 groups, whose
+    //     3-stage ring still fits;
+    //   down: 192 rows for tiles of 2-7 groups (4-5 stages).
+    // Single-group tiles keep the 128-row tiles' deeper rings, and the
+    // others do not fit, so they take a second launch in the same timing
+    // bracket.  Measured on the 8192-token layer: gate/up 5.31 -> 5.08 ms,
+    // down 2.83 -> 2.51 ms; 256-row down tiles (3 stages) took 2.82 ms.
+    // With fewer rows (decode: every tile one group) the second launch is
+    // pure overhead (~16 us), and with more (heavy experts' full tiles next to
+    // light ones) two serial launches lose the single launch's interleaving
+    // (+0.14 ms on the 16384-token skewed layer).
+    const bool typical_partial =
+        (long long)rows_cap >= 32LL * n_ffn && (long long)rows_cap <= 256LL * n_ffn;
+    if (typical_partial && I % 128 == 0) {
+      const int ntw = I / 128;
+      MOE_LAUNCH("ffn_gateup_bf16", s,
+                 ffn_mfma_bf16<true, kBNGateUpWide><<<groups * 8 * ntw, kGemmThreads, 0, s>>>(
+                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
+                     I, H, ntw, kWideGroupsGateUp, (bf16*)hh);
+                 ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
+                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
+                     I, H, nt1, kAllGroups & ~kWideGroupsGateUp, (bf16*)hh));
+    } else {
+      MOE_LAUNCH("ffn_gateup_bf16", s,
+                 ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
+                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
+                     I, H, nt1, kAllGroups, (bf16*)hh));
+    }
+    if (typical_partial && H % kBNWide == 0) {
       const int ntw = H / kBNWide;
       MOE_LAUNCH("ffn_down_bf16", s,
                  ffn_mfma_bf16<false, kBNWide><<<groups * 8 * ntw, kGemmThreads, 0, s>>>(
