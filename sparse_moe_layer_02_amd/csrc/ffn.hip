@@ -50,7 +50,6 @@ constexpr int kBK = 64;                 // k elements per pipeline step
 constexpr int kRowBytes = kBK * 2;      // 128 B per LDS row of a step
 constexpr int kBN = 128;                // weight rows per block (down, partial tiles: 192)
 constexpr int kBNWide = 192;
-constexpr int kAllGroups = 0x1FE;       // bits 1..8: m-tiles of 1-8 32-row groups
 constexpr int kWideGroups = 0x0FC;      // bits 2..7: the down GEMM's 192-row tiles
 constexpr int kBNGateUpWide = 256;      // gate/up: 128 hh columns per tile
 constexpr int kWideGroupsGateUp = 0x03C;   // bits 2..5: 256-row tiles (a 3-stage ring fits)
@@ -394,28 +393,18 @@ constexpr bool ring_fits(int G, int BN) {
   return kLdsBytes / (32 * G * kRowBytes + BN * kRowBytes) >= 3;
 }
 
-// One launch covers the m-tiles whose number of 32-row groups g has bit g
-// set in gmask; the others' blocks exit at once.
+// One block's work: rows [row0, row0 + rows) of expert e against column
+// tile nt (of NT) of BN weight rows.
 template <bool GATEUP, int BN>
-__global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
-    const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
-    const bf16* __restrict__ W, const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-    int KD, int I, int H, int NT, int gmask, bf16* __restrict__ C) {
+__device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A,
+                                          const int32_t* __restrict__ gather, int gK, int gT,
+                                          const bf16* __restrict__ W, int e, int row0, int rows,
+                                          int nt, int NT, int KD, int I, int H,
+                                          bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
   static_assert(BM == 256, "instances cover 8 groups of 32 rows");
   constexpr int CB = BN / 64;   // 16-column MFMA blocks per compute wave (partial tiles)
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-
-  const int b = blockIdx.x;
-  const int xcd = b & 7, slot = b >> 3;
-  const int mt = (slot / NT) * 8 + xcd;
-  const int nt = slot % NT;
-  if (mt >= *ntiles) return;
-  const int4 tile = tiles[mt];
-  const int e = tile.x, row0 = tile.y, rows = tile.z;
   const int groups = (rows + 31) >> 5;
-  if (!((gmask >> groups) & 1)) return;   // another launch's tile
-  if (!ring_fits(groups, BN)) return;     // never launched for (8 groups at BN 192)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
 
@@ -545,6 +534,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     out.flush(C + (size_t)row0 * H + nt * NC, H, rows, threadIdx.x);
 }
 
+// One launch per GEMM.  Block -> (m-tile, column slot), XCD-aware: the slots
+// of one m-tile run on one XCD and share its activation rows through that
+// XCD's L2.  Slots count 128-row column tiles; an m-tile whose number of
+// 32-row groups has its bit set in wide_mask takes the wider tiles (BNW
+// rows) instead, and its slots past N / BNW exit at once -- cheaper than a
+// second launch for the other tiles (measured: an empty second launch cost
+// 57 us, and two serial launches each drain their own tail; gate/up on the
+// 8192-token layer 5.1-5.2 -> 4.55 ms).  WIDE = false compiles the 128-row
+// path alone, for layers with no wide tiles: the kernel with both paths
+// measured 1.5 % slower there (the 16384-token skewed layer's gate/up).
+template <bool GATEUP, bool WIDE>
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
+    const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
+    const bf16* __restrict__ W, const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+    int KD, int I, int H, int NT, int wide_mask, bf16* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  constexpr int BNW = GATEUP ? kBNGateUpWide : kBNWide;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NT) * 8 + xcd;
+  const int nt = slot % NT;
+  if (mt >= *ntiles) return;
+  const int4 tile = tiles[mt];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const int groups = (rows + 31) >> 5;
+  if constexpr (WIDE) {
+    if (((wide_mask >> groups) & 1) && ring_fits(groups, BNW)) {
+      const int ntw = (GATEUP ? 2 * I : H) / BNW;
+      if (nt >= ntw) return;
+      ffn_block<GATEUP, BNW>(smem, A, gather, gK, gT, W, e, row0, rows, nt, ntw, KD, I, H, C);
+      return;
+    }
+  }
+  ffn_block<GATEUP, kBN>(smem, A, gather, gK, gT, W, e, row0, rows, nt, NT, KD, I, H, C);
+}
+
 // ------------------------------------------------------------ fp32 path --
 // Plain LDS-tiled FMA kernels for fp32 layers (exact fp32 products, fp32
 // accumulation); any H and I.  Tile: 32 rows x 32 outputs, K step 32.
@@ -647,45 +672,31 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
     //     3-stage ring still fits;
     //   down: 192 rows for tiles of 2-7 groups (4-5 stages).
     // Single-group tiles keep the 128-row tiles' deeper rings, and the
-    // others do not fit, so they take a second launch in the same timing
-    // bracket.  Measured on the 8192-token layer: gate/up 5.31 -> 5.08 ms,
-    // down 2.83 -> 2.51 ms; 256-row down tiles (3 stages) took 2.82 ms.
-    // With fewer rows (decode: every tile one group) the second launch is
-    // pure overhead (~16 us), and with more (heavy experts' full tiles next to
-    // light ones) two serial launches lose the single launch's interleaving
-    // (+0.14 ms on the 16384-token skewed layer).
+    // others do not fit.  Measured on the 8192-token layer: gate/up 5.31 ->
+    // 5.08 ms, down 2.83 -> 2.51 ms; 256-row down tiles (3 stages) took
+    // 2.82 ms.  With fewer rows (decode: every tile one group) there is
+    // nothing to widen, and with more (heavy experts' full tiles next to
+    // light ones; the 16384-token skewed layer) the wide tiles measured
+    // 0.14 ms slower.
     const bool typical_partial =
         (long long)rows_cap >= 32LL * n_ffn && (long long)rows_cap <= 256LL * n_ffn;
-    if (typical_partial && I % 128 == 0) {
-      const int ntw = I / 128;
-      MOE_LAUNCH("ffn_gateup_bf16", s,
-                 ffn_mfma_bf16<true, kBNGateUpWide><<<groups * 8 * ntw, kGemmThreads, 0, s>>>(
-                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
-                     I, H, ntw, kWideGroupsGateUp, (bf16*)hh);
-                 ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
-                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
-                     I, H, nt1, kAllGroups & ~kWideGroupsGateUp, (bf16*)hh));
+    const int wide_gu = typical_partial && (2 * I) % kBNGateUpWide == 0 ? kWideGroupsGateUp : 0;
+    const int wide_dn = typical_partial && H % kBNWide == 0 ? kWideGroups : 0;
+#define MOE_GEMMS(W)                                                                     \
+    MOE_LAUNCH("ffn_gateup_bf16", s,                                                       \
+               ffn_mfma_bf16<true, W><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(           \
+                   (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, \
+                   I, H, nt1, wide_gu, (bf16*)hh));                                       \
+    MOE_LAUNCH("ffn_down_bf16", s,                                                         \
+               ffn_mfma_bf16<false, W><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(          \
+                   (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, \
+                   nt2, wide_dn, (bf16*)y_perm))
+    if (wide_gu || wide_dn) {
+      MOE_GEMMS(true);
     } else {
-      MOE_LAUNCH("ffn_gateup_bf16", s,
-                 ffn_mfma_bf16<true, kBN><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(
-                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H,
-                     I, H, nt1, kAllGroups, (bf16*)hh));
+      MOE_GEMMS(false);
     }
-    if (typical_partial && H % kBNWide == 0) {
-      const int ntw = H / kBNWide;
-      MOE_LAUNCH("ffn_down_bf16", s,
-                 ffn_mfma_bf16<false, kBNWide><<<groups * 8 * ntw, kGemmThreads, 0, s>>>(
-                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
-                     ntw, kWideGroups, (bf16*)y_perm);
-                 ffn_mfma_bf16<false, kBN><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
-                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
-                     nt2, kAllGroups & ~kWideGroups, (bf16*)y_perm));
-    } else {
-      MOE_LAUNCH("ffn_down_bf16", s,
-                 ffn_mfma_bf16<false, kBN><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(
-                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H,
-                     nt2, kAllGroups, (bf16*)y_perm));
-    }
+#undef MOE_GEMMS
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
     MOE_LAUNCH("ffn_gateup_f32", s,
