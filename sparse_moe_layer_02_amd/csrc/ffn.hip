@@ -664,24 +664,22 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
   if (dtype == MOE_BF16) {
     const unsigned groups = ceil_div(mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
-    // Where the typical expert has one partial m-tile -- 32 to 256 rows per
-    // FFN expert even if every pick went to one, decided from the capacity
-    // -- both GEMMs take wider weight tiles for their partial tiles, which
-    // cut the activation traffic from L2 per weight byte:
+    // Partial m-tiles take wider weight tiles, which cut the activation
+    // traffic from L2 per weight byte:
     //   gate/up: 256 rows (128 hh columns) for tiles of 2-5 groups, whose
     //     3-stage ring still fits;
     //   down: 192 rows for tiles of 2-7 groups (4-5 stages).
     // Single-group tiles keep the 128-row tiles' deeper rings, and the
     // others do not fit.  Measured on the 8192-token layer: gate/up 5.31 ->
-    // 5.08 ms, down 2.83 -> 2.51 ms; 256-row down tiles (3 stages) took
-    // 2.82 ms.  With fewer rows (decode: every tile one group) there is
-    // nothing to widen, and with more (heavy experts' full tiles next to
-    // light ones; the 16384-token skewed layer) the wide tiles measured
-    // 0.14 ms slower.
-    const bool typical_partial =
-        (long long)rows_cap >= 32LL * n_ffn && (long long)rows_cap <= 256LL * n_ffn;
-    const int wide_gu = typical_partial && (2 * I) % kBNGateUpWide == 0 ? kWideGroupsGateUp : 0;
-    const int wide_dn = typical_partial && H % kBNWide == 0 ? kWideGroups : 0;
+    // 5.08 ms and down 2.83 -> 2.51 ms as two launches per GEMM, gate/up
+    // 4.55 ms as one; 256-row down tiles (3 stages) took 2.82 ms.  On the
+    // 16384-token skewed layer (full tiles next to light experts' partial
+    // ones) 0.19 ms faster.  Where the average FFN expert would have under
+    // 32 rows even if every pick went to one (decode), every tile is a
+    // single group and the kernel without the wide path is launched.
+    const bool enough_rows = (long long)rows_cap >= 32LL * n_ffn;
+    const int wide_gu = enough_rows && (2 * I) % kBNGateUpWide == 0 ? kWideGroupsGateUp : 0;
+    const int wide_dn = enough_rows && H % kBNWide == 0 ? kWideGroups : 0;
 #define MOE_GEMMS(W)                                                                     \
     MOE_LAUNCH("ffn_gateup_bf16", s,                                                       \
                ffn_mfma_bf16<true, W><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(           \
