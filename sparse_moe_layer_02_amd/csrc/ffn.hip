@@ -12,9 +12,9 @@
 //     of the weight matrix, so every weight tile is fetched from HBM once when
 //     an expert's rows fit one m-tile -- the regime of the full-scale layer,
 //     where the weights (not the MFMA rate) bound the time.  BN = 128, or,
-//     for the partial tiles of a layer whose experts typically fit one tile,
-//     256 (gate/up) and 192 (down): the activation rows every column tile
-//     re-reads from L2 then cost less per weight byte (see launch_expert_ffn);
+//     chosen per block, 256 (gate/up, partial tiles of 2-5 row groups) and
+//     192 (down, 2-7 groups): the activation rows every column tile re-reads
+//     from L2 then cost less per weight byte (see launch_expert_ffn);
 //   - wave w owns BN / 4 weight rows (16-column MFMA blocks) and every row
 //     block of the m-tile; 32-row groups past the expert's rows are skipped;
 //   - 8 waves: four compute waves (fragment reads + MFMA only) and four
@@ -48,8 +48,8 @@ constexpr int kThreads = 256;        // fp32 path and the small kernels
 constexpr int kGemmThreads = 512;    // bf16 GEMM: 4 compute + 4 loader waves
 constexpr int kBK = 64;                 // k elements per pipeline step
 constexpr int kRowBytes = kBK * 2;      // 128 B per LDS row of a step
-constexpr int kBN = 128;                // weight rows per block (down, partial tiles: 192)
-constexpr int kBNWide = 192;
+constexpr int kBN = 128;                // weight rows per block (the narrow tiles)
+constexpr int kBNWide = 192;            // down: wide tiles
 constexpr int kWideGroups = 0x0FC;      // bits 2..7: the down GEMM's 192-row tiles
 constexpr int kBNGateUpWide = 256;      // gate/up: 128 hh columns per tile
 constexpr int kWideGroupsGateUp = 0x03C;   // bits 2..5: 256-row tiles (a 3-stage ring fits)
