@@ -90,7 +90,8 @@ moe_status moe_route(const float *logits, const float *bias, int T, int E, int K
  *   x_perm[r] = x[t] for the selection (t, k) held by row r, r < S
  *   row_src[r] = t*K + k, r < S
  *   slot_row[t*K + k] = its row, or -1 when it chose an identity expert
- * x: [T][H] (dtype); topk_idx: [T][K] with entries in [0, E); x_perm: capacity
+ * x: [T][H] (dtype); topk_idx: [T][K] with entries in [0, E) (an id outside
+ * [0, n_ffn) is an identity pick: slot_row -1, no row); x_perm: capacity
  * [T*K][H]; row_src: capacity [T*K]; slot_row: [T*K]; offsets: [n_ffn + 1].
  * Rows >= S of x_perm and row_src are left untouched.
  * x_perm may be NULL (and then x too): only offsets, row_src and slot_row are

@@ -30,7 +30,7 @@ __device__ __forceinline__ void build_masks(unsigned long long* mask, const int3
     const int32_t* row = idx + (size_t)t * K;
     for (int k = 0; k < K; ++k) {
       int e = row[k];
-      if (e < n_ffn) atomicOr(&mask[e], 1ull << lane);
+      if ((unsigned)e < (unsigned)n_ffn) atomicOr(&mask[e], 1ull << lane);
     }
   }
   __syncthreads();
@@ -111,12 +111,73 @@ __global__ __launch_bounds__(kWave) void perm_scatter(const int32_t* __restrict_
   for (int k = 0; k < K; ++k) {
     const int s = t * K + k;
     const int e = idx[s];
-    if (e < n_ffn) {
+    if ((unsigned)e < (unsigned)n_ffn) {   // other ids: not an FFN pick
       const int row = offsets[e] + pre[(size_t)e * nblk + blk] + __popcll(mask[e] & below);
       slot_row[s] = row;
       row_src[row] = s;
     } else {
       slot_row[s] = -1;
+    }
+  }
+}
+
+// T <= 64 (decode): the tokens are one 64-token block, so the histogram,
+// both scans and the scatter fit one workgroup -- one launch instead of four
+// (the four cost ~27 us at 64 tokens, almost all launch latency).  Wave 0
+// (lane = token) builds the masks and scatters; all 1024 threads scan the
+// experts.  The rows are those of the general path: offsets[e] +
+// popcount(mask[e] & lanes below).  LDS: n_ffn masks, then n_ffn offsets.
+__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ idx, int T, int K,
+                                                   int n_ffn, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ row_src,
+                                                   int32_t* __restrict__ slot_row) {
+  extern __shared__ unsigned long long mask[];
+  int* off = (int*)(mask + n_ffn);
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n_ffn; e += 1024) mask[e] = 0ull;
+  __syncthreads();
+  if (tid < kWave && tid < T) {
+    const int32_t* row = idx + (size_t)tid * K;
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      if ((unsigned)e < (unsigned)n_ffn) atomicOr(&mask[e], 1ull << tid);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the per-expert counts: a chunk of experts per thread
+  const int per = (n_ffn + 1023) / 1024;
+  const int lo = min(n_ffn, tid * per), hi = min(n_ffn, lo + per);
+  int sum = 0;
+  for (int e = lo; e < hi; ++e) sum += __popcll(mask[e]);
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int e = lo; e < hi; ++e) {
+    off[e] = run;
+    offsets[e] = run;
+    run += __popcll(mask[e]);
+  }
+  if (tid == 1023) offsets[n_ffn] = part[1023];
+  __syncthreads();
+  if (tid < kWave && tid < T) {
+    const unsigned long long below = (1ull << tid) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int s = tid * K + k;
+      const int e = idx[s];
+      if ((unsigned)e < (unsigned)n_ffn) {
+        const int r = off[e] + __popcll(mask[e] & below);
+        slot_row[s] = r;
+        row_src[r] = s;
+      } else {
+        slot_row[s] = -1;
+      }
     }
   }
 }
@@ -179,17 +240,23 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, i
   int32_t* cnt = (int32_t*)ws;
   int32_t* tot = (int32_t*)((char*)ws + align256((size_t)n_ffn * nblk * 4));
   const size_t lds = (size_t)(n_ffn > 0 ? n_ffn : 1) * sizeof(unsigned long long);
-  if (n_ffn > 0) {
-    MOE_LAUNCH("permute_hist", s,
-               perm_hist<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt));
-    MOE_LAUNCH("permute_scan_blocks", s,
-               perm_scan_blocks<<<ceil_div(n_ffn, 4), 256, 0, s>>>(cnt, nblk, n_ffn, tot));
+  if (nblk == 1 && n_ffn > 0) {
+    MOE_LAUNCH("permute_small", s,
+               perm_small<<<1, 1024, (size_t)n_ffn * 12, s>>>(idx, T, K, n_ffn, offsets, row_src,
+                                                              slot_row));
+  } else {
+    if (n_ffn > 0) {
+      MOE_LAUNCH("permute_hist", s,
+                 perm_hist<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt));
+      MOE_LAUNCH("permute_scan_blocks", s,
+                 perm_scan_blocks<<<ceil_div(n_ffn, 4), 256, 0, s>>>(cnt, nblk, n_ffn, tot));
+    }
+    MOE_LAUNCH("permute_scan_experts", s,
+               perm_scan_experts<<<1, 1024, 0, s>>>(tot, n_ffn, offsets));
+    MOE_LAUNCH("permute_scatter", s,
+               perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets,
+                                                     row_src, slot_row));
   }
-  MOE_LAUNCH("permute_scan_experts", s,
-             perm_scan_experts<<<1, 1024, 0, s>>>(tot, n_ffn, offsets));
-  MOE_LAUNCH("permute_scatter", s,
-             perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets,
-                                                   row_src, slot_row));
   if (!x_perm) return hipGetLastError();   // indices only: the GEMM gathers x rows itself
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = (int)((size_t)H * esize / 16);
