@@ -129,30 +129,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   constexpr int kWaves = kRouteThreads / kWave;
-  float bs[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    int e = lane + kWave * i;
-    bs[i] = e < E ? bias[e] : 0.0f;
-  }
+  // the token's logits, for the softmax sum and the gates of its picks: kept
+  // in LDS rather than in registers through the K rounds (94 -> 73 VGPRs at
+  // 12 logits per lane, one more wave per SIMD)
+  __shared__ float lrow[kWaves][kWave * EPL];
   bool bad = false;
   const int t_end = min(T, (blockIdx.x + 1) * kTokensPerBlock);
   for (int t = blockIdx.x * kTokensPerBlock + wave; t < t_end; t += kWaves) {
     const float* lr = logits + (size_t)t * E;
-    float lg[EPL];
     uint64_t cand[EPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       int e = lane + kWave * i;
       if (e < E) {
-        lg[i] = lr[e];
-        float key = lg[i] + bs[i];
-        bad |= (key != key) || !isfinite(lg[i]);
+        const float lg = lr[e];
+        lrow[wave][e] = lg;
+        float key = lg + bias[e];
+        bad |= (key != key) || !isfinite(lg);
         cand[i] = ((uint64_t)key_order(key) << 32) | (uint32_t)(~(uint32_t)e);
-        mx = fmaxf(mx, lg[i]);
+        mx = fmaxf(mx, lg);
       } else {
-        lg[i] = -INFINITY;
         cand[i] = 0;
       }
     }
@@ -161,26 +158,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) part += expf(lg[i] - mx);
+      if (lane + kWave * i < E) part += expf(lrow[wave][lane + kWave * i] - mx);
     const float den = wave_sum_f32(part);
 
+    // the rounds only select: pick k is kept in lane k % 64, and every 64
+    // picks (or at the last) the lanes write them and their gates at once
+    int pick = 0;
     for (int k = 0; k < K; ++k) {
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) best = cand[i] > best ? cand[i] : best;
       best = wave_max_u64(best);
       const int e = (int)(~(uint32_t)best);
-      float mine = 0.0f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i == e) {
-          cand[i] = 0;
-          mine = lg[i];
+        if (lane + kWave * i == e) cand[i] = 0;
+      if (lane == (k & (kWave - 1))) pick = e;
+      if ((k & (kWave - 1)) == kWave - 1 || k == K - 1) {
+        const int base = k & ~(kWave - 1);
+        if (lane <= k - base) {
+          idx[(size_t)t * K + base + lane] = pick;
+          gate[(size_t)t * K + base + lane] = expf(lrow[wave][pick] - mx) / den;
         }
-      const float le = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mine), e & (kWave - 1)));
-      if (lane == 0) {
-        idx[(size_t)t * K + k] = e;
-        gate[(size_t)t * K + k] = expf(le - mx) / den;
       }
     }
   }

@@ -93,6 +93,29 @@ def test_k_equals_e_picks_every_expert():
     _e2e(cfg, inp, buf)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+def test_more_than_64_picks_per_token(path):
+    # K = 70 of E = 96: the routing kernel writes its picks in two chunks of
+    # lanes (64 + 6), and combine takes its general kernel (K > 16)
+    cfg = workload.MoEConfig("k70", T=50, H=128, N=64, Z=32, I=64, K=70, dtype="bf16",
+                             sigma_w=0.05, bias_lo=-0.1, bias_hi=0.1, scale=1.25)
+    inp, buf = _run(cfg, path=path)
+    stage_checks(cfg, inp, buf)
+    assert host(buf["counts"]).sum() == cfg.T * cfg.K
+    _e2e(cfg, inp, buf)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_rows_wider_than_one_pass(path):
+    # H = 8320 > 8 x 1024: combine loops over the row (its one-piece-per-thread
+    # kernel takes rows of at most 8192)
+    cfg = workload.MoEConfig("h8320", T=20, H=8320, N=4, Z=2, I=64, K=3, dtype="bf16",
+                             sigma_w=0.01, bias_lo=-0.1, bias_hi=0.1, scale=1.0)
+    inp, buf = _run(cfg, path=path)
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
+
+
 @pytest.mark.parametrize("T", [40, 300])
 def test_largest_expert_pool(T):
     # E = 1024, the most the routing kernel takes: 16 keys per lane, a
