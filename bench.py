@@ -80,6 +80,10 @@ def parse():
                    help="run the identity experts as their own call (moe_zero_experts into "
                         "y_acc, on a second stream, then moe_combine) instead of inside combine "
                         "(moe_combine_identity)")
+    p.add_argument("--router-split-per-call", action="store_true",
+                   help="split the fp32 router weights into their bf16 planes inside every "
+                        "router call instead of once before the run (moe_router_split_weights, "
+                        "a weight-format preparation outside the timed steps)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -250,6 +254,8 @@ def main():
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
                             grouped_copy=args.grouped_copy,
                             separate_identity=args.separate_identity)
+    if not args.router_split_per_call:
+        moe.prepare_router(inp["w_router"], buf)   # once: the weights do not change
     stream = torch.cuda.current_stream(dev)
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20)
@@ -356,7 +362,9 @@ def main():
                    "zero_experts": cfg.Z, "intermediate": cfg.I, "top_k": cfg.K,
                    "ffn_scale": cfg.scale, "ffn_rows": S, "active_ffn_experts": alg["active"],
                    "dispatch": "grouped_copy" if args.grouped_copy else "row_gather",
-                   "identity_experts": "separate" if args.separate_identity else "in_combine"},
+                   "identity_experts": "separate" if args.separate_identity else "in_combine",
+                   "router_weights": "split_per_call" if args.router_split_per_call
+                   else "presplit_planes"},
         "roofline": roofline,
         "down_gemm": {"kernel_ms": round(d_ms, 4),
                       "hbm_frac": round(alg["down_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -64,6 +64,28 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 moe_status moe_router_logits(const void *x, int x_dtype, const float *w_router,
                              int T, int H, int E, float *logits, void *stream);
 
+/* The router weights' three bf16 planes, split once (the same exact split
+ * moe_router_logits does on every call: w = hi + mid + lo, hi = w truncated
+ * to bf16, mid = the remainder truncated, lo = what is left; Technical Report
+ * notes, Key claims [§2.1]: fp32 router scores).  A weight-format
+ * preparation, to be redone whenever w_router changes.
+ *   w_router [E][H] fp32 (16-byte aligned), w_planes [3][E][H] bf16 (16-byte
+ *   aligned, caller-owned: plane p of expert e at (p*E + e)*H).
+ * H % 8 == 0, E >= 1. */
+moe_status moe_router_split_weights(const float *w_router, int E, int H, void *w_planes,
+                                    void *stream);
+
+/* moe_router_logits with the planes of moe_router_split_weights: bitwise the
+ * same logits (the same matrix-core operations in the same order), without
+ * the split in the kernel where the large-batch tiles run (bf16 x, H % 32 ==
+ * 0, at least 256 tiles of 256 tokens x 96 experts).  w_router is still
+ * required (the other tile shapes split it themselves); w_planes may be
+ * NULL, which is moe_router_logits.  w_planes stale against w_router gives
+ * scores of the weights it was split from. */
+moe_status moe_router_logits_planes(const void *x, int x_dtype, const float *w_router,
+                                    const void *w_planes, int T, int H, int E, float *logits,
+                                    void *stream);
+
 /* Top-K routing with a selection bias (Technical Report notes, Key claims
  * [§2.1.1]: the bias the PID controller adjusts from routing frequency enters
  * selection only).

@@ -30,6 +30,8 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SIGS = {
     "moe_router_logits": ([_P, _I, _P, _I, _I, _I, _P, _P], _I),
+    "moe_router_split_weights": ([_P, _I, _I, _P, _P], _I),
+    "moe_router_logits_planes": ([_P, _I, _P, _P, _I, _I, _I, _P, _P], _I),
     "moe_route": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_permute_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "moe_permute": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
@@ -110,16 +112,50 @@ def _want(t, dtype, name):
 
 # --------------------------------------------------------------- the calls --
 
-def moe_router_logits(x, w_router, logits):
-    """logits[T, E] (fp32) = x[T, H] @ w_router[E, H]^T."""
-    _dev(x, w_router, logits)
+def moe_router_logits(x, w_router, logits, w_planes=None):
+    """logits[T, E] (fp32) = x[T, H] @ w_router[E, H]^T.  w_planes: the
+    router weights' bf16 planes from moe_router_split_weights (bitwise the
+    same logits, without the split inside the large-batch kernel)."""
+    _dev(x, w_router, logits, w_planes)
     _want(w_router, torch.float32, "w_router")
     _want(logits, torch.float32, "logits")
     T, H = x.shape
     E = w_router.shape[0]
     assert w_router.shape == (E, H) and logits.shape == (T, E)
-    _check("moe_router_logits", lib().moe_router_logits(
-        _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
+    if w_planes is None:
+        _check("moe_router_logits", lib().moe_router_logits(
+            _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
+        return
+    _want(w_planes, torch.bfloat16, "w_planes")
+    assert w_planes.shape == (3, E, H)
+    _check("moe_router_logits_planes", lib().moe_router_logits_planes(
+        _ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(w_planes), T, H, E, _ptr(logits),
+        _stream(x)))
+
+
+def moe_router_split_weights(w_router, w_planes):
+    """w_planes[3, E, H] (bf16) = the exact split w = hi + mid + lo of the fp32
+    router weights (a weight-format preparation; redo it when w_router
+    changes)."""
+    _dev(w_router, w_planes)
+    _want(w_router, torch.float32, "w_router")
+    _want(w_planes, torch.bfloat16, "w_planes")
+    E, H = w_router.shape
+    assert w_planes.shape == (3, E, H)
+    _check("moe_router_split_weights", lib().moe_router_split_weights(
+        _ptr(w_router), E, H, _ptr(w_planes), _stream(w_router)))
+
+
+def prepare_router(w_router, buf):
+    """Split the router weights once into buf["w_planes"], which forward()
+    then uses.  Redo it whenever w_router changes."""
+    E, H = w_router.shape
+    planes = buf.get("w_planes")
+    if planes is None or planes.shape != (3, E, H) or planes.device != w_router.device:
+        planes = torch.empty((3, E, H), dtype=torch.bfloat16, device=w_router.device)
+    moe_router_split_weights(w_router, planes)
+    buf["w_planes"] = planes
+    return planes
 
 
 def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
@@ -317,6 +353,7 @@ def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False
                            dtype=torch.uint8, device=device),
         y_acc=torch.empty((T, H), dtype=f32, device=device) if separate_identity else None,
         y=torch.empty((T, H), dtype=dtype, device=device),
+        w_planes=None,   # the router weights' planes, set by prepare_router()
         # six-call path: a second stream (default priority) for the identity
         # experts, and the two events that order it against the current stream
         side_stream=torch.cuda.Stream(device=device) if separate_identity else None,
@@ -341,7 +378,7 @@ def forward(x, w_router, bias, w13, w2, K, ffn_scale, buf):
 
 def _forward_fused(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     n_ffn = w13.shape[0]
-    moe_router_logits(x, w_router, buf["logits"])
+    moe_router_logits(x, w_router, buf["logits"], buf.get("w_planes"))
     moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
               buf["status"])
     _dispatch_and_experts(x, K, n_ffn, w13, w2, buf)
@@ -364,7 +401,7 @@ def _forward_six(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     n_ffn = w13.shape[0]
     main = torch.cuda.current_stream(x.device)
     side = buf["side_stream"]
-    moe_router_logits(x, w_router, buf["logits"])
+    moe_router_logits(x, w_router, buf["logits"], buf.get("w_planes"))
     moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
               buf["status"])
     buf["ev_routed"].record(main)
@@ -400,7 +437,7 @@ def forward_serial(x, w_router, bias, w13, w2, K, ffn_scale, buf):
     if buf["y_acc"] is None:
         return _forward_fused(x, w_router, bias, w13, w2, K, ffn_scale, buf)
     n_ffn = w13.shape[0]
-    moe_router_logits(x, w_router, buf["logits"])
+    moe_router_logits(x, w_router, buf["logits"], buf.get("w_planes"))
     moe_route(buf["logits"], bias, K, buf["topk_idx"], buf["topk_gate"], buf["counts"],
               buf["status"])
     _dispatch_and_experts(x, K, n_ffn, w13, w2, buf)

@@ -42,7 +42,29 @@ moe_status moe_router_logits(const void* x, int x_dtype, const float* w_router, 
   if (T < 1 || H < 1 || E < 1 || !fits_i32((long long)T * E)) return MOE_ERR_SHAPE;
   if (!aligned(x, x_dtype == MOE_BF16 ? 2 : 4) || !aligned(w_router, 4) || !aligned(logits, 4))
     return MOE_ERR_ALIGN;
-  return launched(launch_router_logits(x, x_dtype, w_router, T, H, E, logits,
+  return launched(launch_router_logits(x, x_dtype, w_router, nullptr, T, H, E, logits,
+                                       (hipStream_t)stream));
+}
+
+moe_status moe_router_split_weights(const float* w_router, int E, int H, void* w_planes,
+                                    void* stream) {
+  if (!w_router || !w_planes) return MOE_ERR_NULL;
+  if (E < 1 || H < 1 || H % 8 || (long long)E * H > (1ll << 40)) return MOE_ERR_SHAPE;
+  if (!aligned(w_router, 16) || !aligned(w_planes, 16)) return MOE_ERR_ALIGN;
+  return launched(launch_router_split(w_router, E, H, w_planes, (hipStream_t)stream));
+}
+
+moe_status moe_router_logits_planes(const void* x, int x_dtype, const float* w_router,
+                                    const void* w_planes, int T, int H, int E, float* logits,
+                                    void* stream) {
+  if (!x || !w_router || !logits) return MOE_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || E < 1 || !fits_i32((long long)T * E)) return MOE_ERR_SHAPE;
+  if (w_planes && H % 8) return MOE_ERR_SHAPE;
+  if (!aligned(x, x_dtype == MOE_BF16 ? 2 : 4) || !aligned(w_router, 4) || !aligned(logits, 4) ||
+      !aligned(w_planes, 16))
+    return MOE_ERR_ALIGN;
+  return launched(launch_router_logits(x, x_dtype, w_router, w_planes, T, H, E, logits,
                                        (hipStream_t)stream));
 }
 

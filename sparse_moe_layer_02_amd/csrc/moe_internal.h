@@ -60,8 +60,10 @@ void prof_end(int token, hipStream_t s);
   } while (0)
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----------
-hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int H, int E,
-                                float* logits, hipStream_t s);
+// planes: the weights split by launch_router_split, or NULL (split in the kernel)
+hipError_t launch_router_logits(const void* x, int dtype, const float* w, const void* planes,
+                                int T, int H, int E, float* logits, hipStream_t s);
+hipError_t launch_router_split(const float* w, int E, int H, void* planes, hipStream_t s);
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K,
                         int32_t* idx, float* gate, int32_t* counts, int32_t* status,
                         hipStream_t s);

@@ -14,6 +14,9 @@
 //   from four loader waves into a 5-stage LDS ring; the split happens in
 //   registers on the fragment read.  XCD-aware order: the 12 expert tiles of
 //   one token tile run on one XCD.
+// Large bf16 batches take 256 x 96 tiles (router_wide), and with weights split
+// once beforehand (router_split) the same tiles read the planes instead of
+// splitting (router_wide_planes): bitwise the same logits.
 // bf16 activations with T <= 64 and H % 256 == 0 (decode): 16 experts per
 // block, H split over the block's 8 waves (router_small below).
 // fp32 activations (or H % 64 != 0): an LDS-tiled FMA kernel, 64 tokens x 64
@@ -419,6 +422,177 @@ __global__ __launch_bounds__(kRThreads, 1) void router_wide(const bf16* __restri
   }
 }
 
+// ------------------------------------- wide tiles on pre-split weights --
+// The same tiles and the same matrix-core operations in the same order as
+// router_wide, on weights split once into their three bf16 planes
+// (router_split below: planes[p][e][h], p = hi, mid, lo), so that the
+// compute waves only read fragments and multiply.  A stage is 16 KB of x and
+// 18 KB of planes (288 plane rows of 64 B, swizzled like the x rows); four
+// stages fit.  Loader waves 4-5 stream x (8 loads a step each), waves 6-7 the
+// planes (9 each): each loader waits only on its own loads, so the two
+// operands need no split fill.  Measured on the 8192-token layer: 233 -> 189
+// us (16384 tokens: 441 -> 359 us).
+constexpr int kPBStage = 3 * kWN * kWK * 2;       // 18 KB of planes
+constexpr int kPStageBytes = kWAStage + kPBStage;
+constexpr int kPS = 4;                            // ring stages (136 KB)
+constexpr int kPQa = kWAStage / 1024 / 2;         // x loads per x loader per step (8)
+constexpr int kPQb = kPBStage / 1024 / 2;         // plane loads per plane loader per step (9)
+static_assert(kWM * kWPitch <= kPS * kPStageBytes, "output tile fits the ring");
+static_assert((kPS - 2) * kPQb < 64, "vmcnt range");
+
+template <int Q, class F>
+__device__ __forceinline__ void planes_loader(int KT, F& issue) {
+  for (int kt = 0; kt < kPS - 1; ++kt) issue(kt);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<(kPS - 2) * Q>();   // step kt has landed (in-order completion)
+    lds_barrier();                 // publish it; every wave is done with step kt - 1
+    issue(kt + kPS - 1);           // into the stage step kt - 1 used
+  }
+  wait_vmcnt<0>();
+  lds_barrier();   // the LDS is free for the output tile
+}
+
+// Compute waves.  Eight (two per SIMD, 64 tokens x 48 experts each, so that
+// one wave's fragment reads overlap the other's matrix-core work) measured
+// the same as four: 190 vs 189 us on the 8192-token layer.
+constexpr int kPCW = 4;
+constexpr int kPThreads = (kPCW + 4) * kWave;
+constexpr int kPRows = kWM / (kPCW / 2);           // tokens per compute wave
+__global__ __launch_bounds__(kPThreads, 1) void router_wide_planes(
+    const bf16* __restrict__ x, const bf16* __restrict__ planes, int T, int H, int E, int NTE,
+    float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) char smem[kPS * kPStageBytes];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NTE) * 8 + xcd;   // the expert tiles of a token tile share an XCD
+  const int nt = slot % NTE;
+  const int m0 = mt * kWM, n0 = nt * kWN;
+  if (m0 >= T) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KT = H / kWK;
+  const int k_start = ((nt & 1) * KT) / 2;   // two K offsets by tile parity
+  auto k_of = [&](int kt) {
+    int ks = kt + k_start;
+    ks = ks >= KT ? ks - KT : ks;
+    return kt < KT ? ks * kWK : 0;
+  };
+
+  if (wave >= kPCW + 2) {
+    // instruction q of plane loader l covers plane rows 16 (l + 2q) .. +16
+    // (4 lanes a row; 96 rows a plane, so one plane per instruction)
+    const int l = wave - kPCW - 2;
+    const bf16* src[kPQb];
+#pragma unroll
+    for (int q = 0; q < kPQb; ++q) {
+      const int pr = (l + 2 * q) * 16 + (lane >> 2);
+      const int p = pr / kWN, r = pr - p * kWN;
+      src[q] = planes + ((size_t)p * E + min(n0 + r, E - 1)) * H + swz4(pr, lane & 3) * 8;
+    }
+    auto issue = [&](int kt) {
+      char* sb = smem + (kt % kPS) * kPStageBytes + kWAStage;
+      const int k0 = k_of(kt);
+#pragma unroll
+      for (int q = 0; q < kPQb; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(src[q] + k0),
+                                         (lds_void*)(sb + (l + 2 * q) * 1024), 16, 0, 0);
+    };
+    planes_loader<kPQb>(KT, issue);
+  } else if (wave >= kPCW) {
+    // instruction q of x loader l covers x rows 16 (l + 2q) .. +16
+    const int l = wave - kPCW;
+    const bf16* src[kPQa];
+#pragma unroll
+    for (int q = 0; q < kPQa; ++q) {
+      const int ra = (l + 2 * q) * 16 + (lane >> 2);
+      src[q] = x + (size_t)min(m0 + ra, T - 1) * H + swz4(ra, lane & 3) * 8;
+    }
+    auto issue = [&](int kt) {
+      char* sb = smem + (kt % kPS) * kPStageBytes;
+      const int k0 = k_of(kt);
+#pragma unroll
+      for (int q = 0; q < kPQa; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(src[q] + k0),
+                                         (lds_void*)(sb + (l + 2 * q) * 1024), 16, 0, 0);
+    };
+    planes_loader<kPQa>(KT, issue);
+  } else {
+    constexpr int RB = kPRows / 16;
+    const int wr = wave >> 1, wc = wave & 1;
+    f32x4 acc[RB][3];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+    for (int kt = 0; kt < KT; ++kt) {
+      lds_barrier();
+      const char* As = smem + (kt % kPS) * kPStageBytes;
+      const char* Bs = As + kWAStage;
+      const int c = lane >> 4;   // k elements 8c .. 8c + 8 of the step
+      bf16x8 bp[3][3];           // [plane][column block]
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int cb = 0; cb < 3; ++cb) {
+          const int pr = p * kWN + 48 * wc + 16 * cb + (lane & 15);
+          bp[p][cb] = *(const bf16x8*)(Bs + pr * 64 + swz4(pr, c) * 16);
+        }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rA = kPRows * wr + 16 * rb + (lane & 15);
+        const bf16x8 a = *(const bf16x8*)(As + rA * 64 + swz4(rA, c) * 16);
+#pragma unroll
+        for (int cb = 0; cb < 3; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[2][cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[1][cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp[0][cb], acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();   // loads landed, fragments read: the LDS is free
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = kPRows * wr + 16 * rb + 4 * (lane >> 4) + i;
+          *(float*)(smem + r * kWPitch + (48 * wc + 16 * cb + (lane & 15)) * 4) = acc[rb][cb][i];
+        }
+  }
+  lds_barrier();   // the output tile is complete
+  const bool full = n0 + kWN <= E && (E & 3) == 0 && ((uintptr_t)logits & 15) == 0;
+  constexpr int kQuads = kWN / 4;
+  for (int j = threadIdx.x; j < kWM * kQuads; j += kPThreads) {
+    const int r = j / kQuads, cq = j - r * kQuads;
+    if (m0 + r >= T) continue;
+    const f32x4 v = *(const f32x4*)(smem + r * kWPitch + cq * 16);
+    float* dst = logits + (size_t)(m0 + r) * E + n0 + 4 * cq;
+    if (full) {
+      *(f32x4*)dst = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n0 + 4 * cq + u < E) dst[u] = v[u];
+    }
+  }
+}
+
+// planes[p][e][h] (p = hi, mid, lo) of the fp32 router weights, split3 of
+// every 8 consecutive weights of a row (H % 8 == 0).
+__global__ __launch_bounds__(256) void router_split(const float* __restrict__ w, long long n8,
+                                                    long long plane, bf16* __restrict__ planes) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 v0 = *(const f32x4*)(w + 8 * i);
+  const f32x4 v1 = *(const f32x4*)(w + 8 * i + 4);
+  bf16x8 hi, mid, lo;
+  split3(v0, v1, hi, mid, lo);
+  *(bf16x8*)(planes + 8 * i) = hi;
+  *(bf16x8*)(planes + plane + 8 * i) = mid;
+  *(bf16x8*)(planes + 2 * plane + 8 * i) = lo;
+}
+
 // ------------------------------------------------- few tokens (decode) --
 // With T <= 64 the 128 x 64 tiles above leave a dozen blocks for the whole
 // chip, each streaming 64 experts' weights over all of H.  Here a block takes
@@ -494,8 +668,16 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void router_small(const bf16* 
 
 }  // namespace
 
-hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int H, int E,
-                                float* logits, hipStream_t s) {
+hipError_t launch_router_split(const float* w, int E, int H, void* planes, hipStream_t s) {
+  const long long n8 = (long long)E * H / 8;
+  MOE_LAUNCH("router_split", s,
+             router_split<<<(unsigned)ceil_div(n8, 256), 256, 0, s>>>(w, n8, (long long)E * H,
+                                                                      (bf16*)planes));
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const void* x, int dtype, const float* w, const void* planes,
+                                int T, int H, int E, float* logits, hipStream_t s) {
   if (dtype == MOE_BF16 && T <= kSmallT && H % (kSmallWaves * 32) == 0) {
     MOE_LAUNCH("router_logits", s,
                router_small<<<ceil_div(E, kSmallN), kSmallWaves * kWave, 0, s>>>(
@@ -506,6 +688,12 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
       (long long)ceil_div(T, kWM) * ceil_div(E, kWN) >= 256) {   // enough wide tiles for every CU
     const int nte = (E + kWN - 1) / kWN;
     const unsigned groups = ceil_div(ceil_div(T, kWM), 8);
+    if (planes) {
+      MOE_LAUNCH("router_logits", s,
+                 router_wide_planes<<<groups * 8 * nte, kPThreads, 0, s>>>(
+                     (const bf16*)x, (const bf16*)planes, T, H, E, nte, logits));
+      return hipGetLastError();
+    }
     MOE_LAUNCH("router_logits", s,
                router_wide<<<groups * 8 * nte, kRThreads, 0, s>>>((const bf16*)x, w, T, H, E,
                                                                   nte, logits));

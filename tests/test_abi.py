@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -56,6 +56,23 @@ def test_router_logits_validation():
     assert f(FAKE, 1, FAKE, 0, 64, 8, FAKE, None) == SHAPE
     assert f(FAKE, 1, FAKE, 4, 64, 0, FAKE, None) == SHAPE
     assert f(P(0x10001), 1, FAKE, 4, 64, 8, FAKE, None) == ALIGN
+
+
+def test_router_planes_validation():
+    split = moe.lib().moe_router_split_weights
+    assert split(None, 8, 64, FAKE, None) == NULL
+    assert split(FAKE, 8, 64, None, None) == NULL
+    assert split(FAKE, 0, 64, FAKE, None) == SHAPE
+    assert split(FAKE, 8, 60, FAKE, None) == SHAPE          # H % 8
+    assert split(P(0x10004), 8, 64, FAKE, None) == ALIGN    # 16-byte vectors
+    assert split(FAKE, 8, 64, P(0x10008), None) == ALIGN
+    f = moe.lib().moe_router_logits_planes
+    assert f(None, 1, FAKE, FAKE, 4, 64, 8, FAKE, None) == NULL
+    assert f(FAKE, 1, None, FAKE, 4, 64, 8, FAKE, None) == NULL   # w_router stays required
+    assert f(FAKE, 5, FAKE, FAKE, 4, 64, 8, FAKE, None) == DTYPE
+    assert f(FAKE, 1, FAKE, FAKE, 0, 64, 8, FAKE, None) == SHAPE
+    assert f(FAKE, 1, FAKE, FAKE, 4, 60, 8, FAKE, None) == SHAPE  # planes need H % 8
+    assert f(FAKE, 1, FAKE, P(0x10008), 4, 64, 8, FAKE, None) == ALIGN
 
 
 def test_route_validation():
