@@ -19,8 +19,9 @@
 // splitting (router_wide_planes): bitwise the same logits.
 // bf16 activations with T <= 64 and H % 256 == 0 (decode): 16 experts per
 // block, H split over the block's 8 waves (router_small below).
-// fp32 activations (or H % 64 != 0): an LDS-tiled FMA kernel, 64 tokens x 64
-// experts per block, K step 16, a 4x4 patch per thread.  Any T, E, H.
+// fp32 activations (or H % 64 != 0, or x or the weights not 16-byte aligned):
+// an LDS-tiled FMA kernel, 64 tokens x 64 experts per block, K step 16, a 4x4
+// patch per thread.  Any T, E, H.
 #include "moe_internal.h"
 
 namespace moe {
@@ -678,13 +679,16 @@ hipError_t launch_router_split(const float* w, int E, int H, void* planes, hipSt
 
 hipError_t launch_router_logits(const void* x, int dtype, const float* w, const void* planes,
                                 int T, int H, int E, float* logits, hipStream_t s) {
-  if (dtype == MOE_BF16 && T <= kSmallT && H % (kSmallWaves * 32) == 0) {
+  // the matrix-core kernels move x and the weights in 16-byte pieces; other
+  // alignments (the API takes element-aligned pointers) go to the FMA kernel
+  const bool mfma = dtype == MOE_BF16 && (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
+  if (mfma && T <= kSmallT && H % (kSmallWaves * 32) == 0) {
     MOE_LAUNCH("router_logits", s,
                router_small<<<ceil_div(E, kSmallN), kSmallWaves * kWave, 0, s>>>(
                    (const bf16*)x, w, T, H, E, logits));
     return hipGetLastError();
   }
-  if (dtype == MOE_BF16 && H % kWK == 0 &&
+  if (mfma && H % kWK == 0 &&
       (long long)ceil_div(T, kWM) * ceil_div(E, kWN) >= 256) {   // enough wide tiles for every CU
     const int nte = (E + kWN - 1) / kWN;
     const unsigned groups = ceil_div(ceil_div(T, kWM), 8);
@@ -699,7 +703,7 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, const 
                                                                   nte, logits));
     return hipGetLastError();
   }
-  if (dtype == MOE_BF16 && H % kRK == 0) {
+  if (mfma && H % kRK == 0) {
     const int nte = (E + kRN - 1) / kRN;
     const unsigned groups = ceil_div(ceil_div(T, kRM), 8);
     MOE_LAUNCH("router_logits", s,

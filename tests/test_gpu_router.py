@@ -78,3 +78,31 @@ def test_router_split_is_exact(E, H):
     hi_bits = wp[0].cpu().view(torch.int16).numpy().astype(np.uint16)
     w_bits = (w.view(torch.int32).numpy().astype(np.uint32) >> 16).astype(np.uint16)
     np.testing.assert_array_equal(hi_bits, w_bits)
+
+
+@pytest.mark.parametrize("T,E,H", [(40, 100, 512), (700, 130, 320), (6000, 1003, 288)])
+def test_router_logits_misaligned_pointers(T, E, H):
+    # x and w_router offset by 4 bytes from a 16-byte boundary (the API takes
+    # element-aligned pointers): the matrix-core kernels move 16-byte pieces,
+    # so these shapes go to the FMA kernel and must still match the oracle
+    dev = device()
+    print(f"\n[case] router misaligned T={T} E={E} H={H}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(T + E + H)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w = torch.randn(E, H, generator=g) * 0.02
+    xb = torch.zeros(T * H + 8, dtype=torch.bfloat16, device=dev)
+    wb = torch.zeros(E * H + 4, dtype=torch.float32, device=dev)
+    xd = xb[2:2 + T * H].view(T, H)
+    wd = wb[1:1 + E * H].view(E, H)
+    xd.copy_(x)
+    wd.copy_(w)
+    assert xd.data_ptr() % 16 == 4 and wd.data_ptr() % 16 == 4
+    logits = torch.full((T, E), float("nan"), device=dev)
+    moe.moe_router_logits(xd, wd, logits)
+    torch.cuda.synchronize()
+    rows = np.arange(min(T, 64))
+    got = host(logits).astype(np.float64)[rows]
+    xs, wn = x.float().numpy()[rows], w.numpy()
+    ref = oracle.router_logits(xs, wn, threads=THREADS)
+    bound = H * 2.0 ** -24 * (np.abs(xs).astype(np.float64) @ np.abs(wn).astype(np.float64).T)
+    assert (np.abs(got - ref) <= bound + 1e-30).all()
