@@ -43,8 +43,8 @@ MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 CALLS = {
     "moe_router_logits": ("router_logits",),
     "moe_route": ("route_topk", "route_hist"),
-    "moe_permute": ("permute_hist", "permute_scan_blocks", "permute_scan_experts",
-                    "permute_scatter", "permute_gather"),
+    "moe_permute": ("permute_small", "permute_hist", "permute_scan_blocks",
+                    "permute_scan_experts", "permute_scatter", "permute_gather"),
     "moe_expert_ffn": ("ffn_tiles", "ffn_gateup_bf16", "ffn_down_bf16", "ffn_gateup_f32",
                        "ffn_down_f32"),
     "moe_zero_experts": ("zero_experts",),

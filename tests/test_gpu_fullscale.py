@@ -49,6 +49,7 @@ def test_full_scale_layer(name, shared_weights):
     inp = dict(x=workload.make_x(cfg).to(dev), w_router=wr,
                bias=workload.make_bias(cfg).to(dev), w13=w13, w2=w2)
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev)
+    moe.prepare_router(wr, buf)   # the configuration bench.py times: router weights split once
     forward(cfg, inp, buf)
     K, N, tol = cfg.K, cfg.N, TOL[cfg.dtype]
     x_t = inp["x"]
