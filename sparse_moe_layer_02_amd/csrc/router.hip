@@ -17,8 +17,8 @@
 // Large bf16 batches take 256 x 96 tiles (router_wide), and with weights split
 // once beforehand (router_split) the same tiles read the planes instead of
 // splitting (router_wide_planes): bitwise the same logits.
-// bf16 activations with T <= 64 and H % 256 == 0 (decode): 16 experts per
-// block, H split over the block's 8 waves (router_small below).
+// bf16 activations with T <= 64 and H % 256 == 0 (decode): 16 experts x 16
+// tokens per block, H split over the block's 8 waves (router_small below).
 // fp32 activations (or H % 64 != 0, or x or the weights not 16-byte aligned):
 // an LDS-tiled FMA kernel, 64 tokens x 64 experts per block, K step 16, a 4x4
 // patch per thread.  Any T, E, H.
@@ -602,68 +602,70 @@ __global__ __launch_bounds__(256) void router_split(const float* __restrict__ w,
 // inside the block), splits the weights into the three bf16 planes and
 // accumulates; the 8 partial tiles are then added through LDS in wave order,
 // a fixed order, so the result is bitwise reproducible.
-constexpr int kSmallT = 64;       // tokens per block: all of them
+constexpr int kSmallT = 64;       // the most tokens this kernel takes
+constexpr int kSmallTB = 16;      // tokens per block (one MFMA row block)
 constexpr int kSmallN = 16;       // experts per block
 constexpr int kSmallWaves = 8;    // K ranges
 constexpr int kSmallU = 4;        // 32-element k slices in flight per wave
 
+// Block = 16 experts x 16 tokens; its 8 waves each own one eighth of H, and
+// their partial tiles are added through LDS in a fixed order.  The token
+// groups of one expert tile run on one XCD (blockIdx mod 8), so the
+// weights are fetched from HBM once and re-read from L2.  At 64 tokens x
+// 768 experts that is 192 blocks; one block per 16 experts (all 64 tokens,
+// 48 blocks) left most CUs idle: 38 -> 21 us.  Sixteen waves per block
+// (half the K range each) measured slower (22.7 vs 20.5 us).
 __global__ __launch_bounds__(kSmallWaves * kWave) void router_small(const bf16* __restrict__ x,
                                                                     const float* __restrict__ w,
-                                                                    int T, int H, int E,
+                                                                    int T, int H, int E, int NTE,
+                                                                    int NQ,
                                                                     float* __restrict__ logits) {
-  __shared__ float part[kSmallWaves][kSmallT][kSmallN];
-  const int n0 = blockIdx.x * kSmallN;
+  __shared__ float part[kSmallWaves][kSmallTB][kSmallN];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int tq = slot % NQ, nt = (slot / NQ) * 8 + xcd;
+  if (nt >= NTE) return;
+  const int n0 = nt * kSmallN, t0 = tq * kSmallTB;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int kr = H / kSmallWaves;   // a multiple of 32 (H % 256 == 0)
   const int kbeg = wave * kr;
   // v_mfma_f32_16x16x32_bf16 fragments: lane l holds row / column l & 15 and
-  // k elements 8 (l >> 4) .. + 8 of a 32-element slice.  Rows past T and
+  // k elements 8 (l >> 4) .. + 8 of a 32-element slice.  Tokens past T and
   // experts past E are clamped and their results dropped.
   const float* wrow = w + (size_t)min(n0 + (lane & 15), E - 1) * H + kbeg + 8 * (lane >> 4);
-  const bf16* xrow[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-    xrow[rb] = x + (size_t)min(16 * rb + (lane & 15), T - 1) * H + kbeg + 8 * (lane >> 4);
-  f32x4 acc[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+  const bf16* xrow = x + (size_t)min(t0 + (lane & 15), T - 1) * H + kbeg + 8 * (lane >> 4);
+  f32x4 acc = f32x4{0, 0, 0, 0};
   for (int k = 0; k < kr; k += 32 * kSmallU) {
     f32x4 w0[kSmallU], w1[kSmallU];
-    bf16x8 xa[kSmallU][4];
+    bf16x8 xa[kSmallU];
 #pragma unroll
     for (int u = 0; u < kSmallU; ++u) {
       const int kk = min(k + 32 * u, kr - 32);   // past the range: a valid slice, not used
       w0[u] = *(const f32x4*)(wrow + kk);
       w1[u] = *(const f32x4*)(wrow + kk + 4);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) xa[u][rb] = *(const bf16x8*)(xrow[rb] + kk);
+      xa[u] = *(const bf16x8*)(xrow + kk);
     }
 #pragma unroll
     for (int u = 0; u < kSmallU; ++u) {
       if (k + 32 * u >= kr) break;   // wave-uniform
       bf16x8 bh, bm, bl;
       split3(w0[u], w1[u], bh, bm, bl);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bl, acc[rb], 0, 0, 0);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bm, acc[rb], 0, 0, 0);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][rb], bh, acc[rb], 0, 0, 0);
-      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u], bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u], bm, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u], bh, acc, 0, 0, 0);
     }
   }
-  // acc[rb] element i: token 16 rb + 4 (l >> 4) + i, expert n0 + (l & 15)
+  // acc element i: token t0 + 4 (l >> 4) + i, expert n0 + (l & 15)
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][16 * rb + 4 * (lane >> 4) + i][lane & 15] = acc[rb][i];
+  for (int i = 0; i < 4; ++i) part[wave][4 * (lane >> 4) + i][lane & 15] = acc[i];
   __syncthreads();
-  for (int j = threadIdx.x; j < kSmallT * kSmallN; j += kSmallWaves * kWave) {
+  for (int j = threadIdx.x; j < kSmallTB * kSmallN; j += kSmallWaves * kWave) {
     const int t = j / kSmallN, c = j % kSmallN;
     float sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < kSmallWaves; ++v) sum += part[v][t][c];
-    if (t < T && n0 + c < E) logits[(size_t)t * E + n0 + c] = sum;
+    if (t0 + t < T && n0 + c < E) logits[(size_t)(t0 + t) * E + n0 + c] = sum;
   }
 }
 
@@ -683,9 +685,10 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, const 
   // alignments (the API takes element-aligned pointers) go to the FMA kernel
   const bool mfma = dtype == MOE_BF16 && (((uintptr_t)x | (uintptr_t)w) & 15) == 0;
   if (mfma && T <= kSmallT && H % (kSmallWaves * 32) == 0) {
+    const int nte = ceil_div(E, kSmallN), nq = ceil_div(T, kSmallTB);
     MOE_LAUNCH("router_logits", s,
-               router_small<<<ceil_div(E, kSmallN), kSmallWaves * kWave, 0, s>>>(
-                   (const bf16*)x, w, T, H, E, logits));
+               router_small<<<8 * nq * ceil_div(nte, 8), kSmallWaves * kWave, 0, s>>>(
+                   (const bf16*)x, w, T, H, E, nte, nq, logits));
     return hipGetLastError();
   }
   if (mfma && H % kWK == 0 &&
