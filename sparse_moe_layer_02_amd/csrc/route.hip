@@ -4,8 +4,8 @@
 // unbiased logits at the picks; counts is the routing-frequency histogram.
 //
 // One wave64 per token.  Lane l holds experts e = l + 64*i (i < EPL).  Each
-// candidate is packed into one 64-bit integer whose unsigned order is the
-// selection order:
+// candidate is one 64-bit integer whose unsigned order is the selection order
+// (a lane keeps only the high words and forms the integer of its best):
 //   high 32 bits: the fp32 key mapped to an order-preserving integer
 //                 (-0.0 folded onto +0.0; NaN below -inf),
 //   low 32 bits : ~e, so that on equal keys the lower expert id is larger.
@@ -137,7 +137,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int t_end = min(T, (blockIdx.x + 1) * kTokensPerBlock);
   for (int t = blockIdx.x * kTokensPerBlock + wave; t < t_end; t += kWaves) {
     const float* lr = logits + (size_t)t * E;
-    uint64_t cand[EPL];
+    // the candidates' key words; the low word ~e of candidate i follows
+    // from lane and i, so it is formed only for the lane's best
+    uint32_t kq[EPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -147,10 +149,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         lrow[wave][e] = lg;
         float key = lg + bias[e];
         bad |= (key != key) || !isfinite(lg);
-        cand[i] = ((uint64_t)key_order(key) << 32) | (uint32_t)(~(uint32_t)e);
+        kq[i] = key_order(key);
         mx = fmaxf(mx, lg);
       } else {
-        cand[i] = 0;
+        kq[i] = 0;
       }
     }
     // softmax statistics over the unbiased logits (fixed reduction order)
@@ -165,14 +167,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     // picks (or at the last) the lanes write them and their gates at once
     int pick = 0;
     for (int k = 0; k < K; ++k) {
-      uint64_t best = 0;
+      // the lane's best: the largest key word, the lowest i among equal ones
+      uint32_t bk = 0;
+      int bi = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) best = cand[i] > best ? cand[i] : best;
-      best = wave_max_u64(best);
+      for (int i = 0; i < EPL; ++i)
+        if (kq[i] > bk) {
+          bk = kq[i];
+          bi = i;
+        }
+      const uint64_t mine =
+          bk ? ((uint64_t)bk << 32) | (uint32_t)(~(uint32_t)(lane + kWave * bi)) : 0ull;
+      const uint64_t best = wave_max_u64(mine);
       const int e = (int)(~(uint32_t)best);
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i == e) cand[i] = 0;
+        if (lane + kWave * i == e) kq[i] = 0;
       if (lane == (k & (kWave - 1))) pick = e;
       if ((k & (kWave - 1)) == kWave - 1 || k == K - 1) {
         const int base = k & ~(kWave - 1);
