@@ -58,9 +58,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * claims [§2.1, §2.4]: the router picks from one pool of FFN + zero experts).
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h], fp32 result.
  * x: [T][H] in x_dtype; w_router: [E][H] fp32; logits: [T][E] fp32.
- * Any T, E, H >= 1.  With bf16 x and H % 64 == 0 the scores run on bf16
- * matrix cores with w_router split exactly into three bf16 planes (every
- * product exact, fp32 accumulation); otherwise on fp32 FMA. */
+ * Any T, E, H >= 1; x and w_router element-aligned.  With bf16 x, H % 64 ==
+ * 0 and x and w_router 16-byte aligned, the scores run on bf16 matrix cores
+ * with w_router split exactly into three bf16 planes (every product exact,
+ * fp32 accumulation); otherwise on fp32 FMA. */
 moe_status moe_router_logits(const void *x, int x_dtype, const float *w_router,
                              int T, int H, int E, float *logits, void *stream);
 
