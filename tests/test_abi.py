@@ -239,3 +239,13 @@ def test_router_similarity_validation():
     assert f(*a) == ALIGN
     a = list(args); a[6] = need - 1
     assert f(*a) == WS
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback: without the shared library every call raises
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.moe_permute_workspace_bytes(64, 12, 512)
