@@ -424,15 +424,15 @@ __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A
   // rows are all live at once and crowd L2.  Tiles start their K sweep (and
   // wrap around) at one of a few offsets, by column tile: four for full
   // 256-row tiles (3 MB of activation rows), two for the partial tiles of
-  // gate/up (~1.5 MB at the prefill shape) and for down's 192-row tiles
-  // (measured 1.4 % faster than one; one or four for gate/up's 256-row tiles
-  // were slower or equal), and one for down's other partial tiles, whose
-  // m-tile is a few hundred KB.  Measured against one offset per
+  // gate/up (~1.5 MB at the prefill shape; one, three or four were slower or
+  // equal), four for down's 192-row tiles (2.57 -> 2.54 ms on prefill
+  // against two, which was 1.4 % faster than one), and one for down's other
+  // partial tiles, whose m-tile is a few hundred KB.  Measured against one offset per
   // column tile: prefill gate/up 5.38 -> 5.23 ms, down 2.90 -> 2.88 ms, and
   // 7-14 % on experts of 2048-16384 rows.  Tiles of one 32-row group (decode)
   // keep one offset per column tile, which measured 0.4 % faster there.
   const int KT = KD / kBK;
-  const int n_start = rows == kBmBf16 ? 4 : rows <= 32 ? NT : (GATEUP || BN != kBN ? 2 : 1);
+  const int n_start = rows == kBmBf16 ? 4 : rows <= 32 ? NT : GATEUP ? 2 : BN != kBN ? 4 : 1;
   const int k_start = ((nt % n_start) * KT) / n_start;
 
   if (wave >= 4) {   // loader waves
