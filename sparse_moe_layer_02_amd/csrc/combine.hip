@@ -9,7 +9,9 @@
 // reproducible.  Outputs are stored non-temporally: streamed to HBM as they
 // are written rather than left dirty in the caches to be written back during
 // the next kernel's reads (measured: ~0.15 ms less per layer over every
-// kernel that writes rows).
+// kernel that writes rows).  The y_perm rows, each read once, are loaded
+// non-temporally too: 188 -> 157 us on the 8192-token layer, 340 -> 318 us on
+// the 16384-token one.
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,8 +28,17 @@ template <> struct Vec8<bf16> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
   }
-  using Raw = bf16x8;   // a piece as loaded, converted only where it is used
-  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return *(const Raw*)p; }
+  // a piece read once (a y_perm row), loaded non-temporally and converted
+  // only where it is used
+  using Raw = bf16x8;
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) {
+    return __builtin_nontemporal_load((const Raw*)p);
+  }
+  static __device__ __forceinline__ void load_nt(const bf16* p, float* o) {
+    const Raw v = load_raw(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+  }
   static __device__ __forceinline__ float at(const Raw& r, int i) { return (float)r[i]; }
   static __device__ __forceinline__ void store(bf16* p, const float* o) {
     bf16x8 v;
@@ -44,7 +55,13 @@ template <> struct Vec8<float> {
   }
   struct Raw { f32x4 a, b; };
   static __device__ __forceinline__ Raw load_raw(const float* p) {
-    return Raw{*(const f32x4*)p, *(const f32x4*)(p + 4)};
+    return Raw{__builtin_nontemporal_load((const f32x4*)p),
+               __builtin_nontemporal_load((const f32x4*)(p + 4))};
+  }
+  static __device__ __forceinline__ void load_nt(const float* p, float* o) {
+    const Raw v = load_raw(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = v.a[i]; o[4 + i] = v.b[i]; }
   }
   static __device__ __forceinline__ float at(const Raw& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
   static __device__ __forceinline__ void store(float* p, const float* o) {
@@ -164,7 +181,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
       float v[kBatch][8];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (j0 + u < n) Vec8<T>::load(y_perm + (size_t)sl.rows[j0 + u] * H + c, v[u]);
+        if (j0 + u < n) Vec8<T>::load_nt(y_perm + (size_t)sl.rows[j0 + u] * H + c, v[u]);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (j0 + u >= n) break;
