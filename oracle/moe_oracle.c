@@ -36,8 +36,9 @@
 
 /* ---- router scores -------------------------------------------------------
  * logits[t][e] = sum_h x[t][h] * wr[e][h]   (fp64, h ascending)
- * "the router selects K=12 experts per token from a pool of 512 FFN + 256
- * zero-computation experts" -- Technical Report notes, Key claims [§2.1, §2.4]. */
+ * One score per expert of the whole pool, FFN and zero-computation experts
+ * alike (K = 12 of 512 + 256 at full scale): Technical Report notes, Key
+ * claims [§2.1, §2.4]. */
 void oracle_router_logits(const float *x, const float *wr, int T, int H, int E,
                           double *logits)
 {
@@ -230,9 +231,9 @@ void oracle_combine(const double *y_perm, const int32_t *slot_row,
 }
 
 /* ---- bias controller -----------------------------------------------------
- * Per FFN expert i (identity experts' biases are never touched -- Technical
- * Report notes, Key claims [§2.1.1, §2.1.2]: "the PID update excludes
- * zero-computation experts"):
+ * Per FFN expert i (identity experts' biases are never touched: the notes
+ * leave zero-computation experts out of the bias updates -- Technical Report
+ * notes, Key claims [§2.1.1, §2.1.2]):
  *   err_i      = target / n_ffn - counts[i] / T
  *                (the expert's routing frequency below its share of the
  *                target number of activated FFN experts per token; summed
@@ -240,9 +241,9 @@ void oracle_combine(const double *y_perm, const int32_t *slot_row,
  *   integral_i = integral_i + err_i
  *   bias_i     = bias_i + kp * err_i + ki * integral_i + kd * (err_i - prev_i)
  *   prev_i     = err_i
- * The report's controller adjusts each FFN expert's bias from token-routing
- * frequency, refining the aux-loss-free update (bias += step * sign(error)),
- * to hold the average number of activated FFN experts at a target
+ * The report's controller moves each FFN expert's bias by how often tokens
+ * route to it, a refinement of the aux-loss-free update (bias += step *
+ * sign(error)), so that the mean count of activated FFN experts holds a target
  * (Key claims [§2.1.1], Method).  The error, the increment form and the gains
  * are not on the pages: this is the plainest reading (the aux-loss-free
  * update with sign(err) replaced by a PID of err).  State in fp64. */

@@ -240,15 +240,17 @@ def _tiny(seed=0, T=48, H=32, N=6, Z=3, I=8, K=3):
     return x, wr, b, w13, w2, K
 
 
-def _brute_force(x, wr, b, w13, w2, K, s):
+def _brute_force(x, wr, b, w13, w2, K, s, sel=None):
     """Per token, loop over every expert of the pool with weight 0 for the
     unpicked ones.  Library pieces: BLAS matmul, a stable sort, scipy's
-    softmax and logistic function."""
+    softmax and logistic function.  sel [T, K]: the experts each token
+    keeps (default: the top K of the fp32 keys)."""
     N = w13.shape[0]
     I = w2.shape[2]
     E = wr.shape[0]
     l32 = (x.astype(np.float64) @ wr.astype(np.float64).T).astype(np.float32)
-    sel = _lib_topk(l32, b, K)
+    if sel is None:
+        sel = _lib_topk(l32, b, K)
     p = sp.softmax(l32.astype(np.float64), axis=1)
     y = np.zeros(x.shape, np.float64)
     for t in range(x.shape[0]):
@@ -271,6 +273,45 @@ def test_layer_matches_brute_force(seed, s):
     got = oracle.layer(x, wr, b, w13, w2, K, s)["y"]
     ref = _brute_force(x, wr, b, w13, w2, K, s)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_layer_with_routing_on_the_oracles_own_choice_is_the_layer():
+    # the flip-rule reference row, fed the choice the oracle made itself,
+    # must be the oracle's layer output bit for bit
+    x, wr, b, w13, w2, K = _tiny(7)
+    ref = oracle.layer(x, wr, b, w13, w2, K, 1.3)
+    got = oracle.layer_with_routing(x, ref["logits32"], ref["idx"], w13, w2, 1.3)
+    np.testing.assert_array_equal(got, ref["y"])
+
+
+def test_layer_with_routing_follows_a_swapped_expert_set():
+    # Technical Report notes, Key claims [§2.1]: the output is the gate-weighted
+    # sum over the experts a token keeps.  Swap, for some tokens, the K-th
+    # pick for the first unpicked expert (an FFN expert for one token, an
+    # identity expert for another) and compare with brute force over the
+    # pool restricted to the swapped sets.
+    x, wr, b, w13, w2, K = _tiny(8, T=20, N=6, Z=3, K=3)
+    N = w13.shape[0]
+    ref = oracle.layer(x, wr, b, w13, w2, K, 0.8)
+    key = (ref["logits32"] + b[None, :]).astype(np.float32)
+    sel = ref["idx"].copy()
+    order = np.argsort(-key, axis=1, kind="stable")
+    swapped_to = {}
+    for t in range(x.shape[0]):
+        nxt = order[t, K]                      # the best expert the token did not keep
+        kind = "ffn" if nxt < N else "identity"
+        if kind not in swapped_to:
+            sel[t, K - 1] = nxt
+            swapped_to[kind] = t
+    assert set(swapped_to) == {"ffn", "identity"}
+    got = oracle.layer_with_routing(x, ref["logits32"], sel, w13, w2, 0.8)
+    want = _brute_force(x, wr, b, w13, w2, K, 0.8, sel=sel)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # the swapped tokens really changed, the others did not
+    for t in swapped_to.values():
+        assert np.abs(got[t] - ref["y"][t]).max() > 1e-6
+    keep = np.setdiff1d(np.arange(x.shape[0]), list(swapped_to.values()))
+    np.testing.assert_array_equal(got[keep], ref["y"][keep])
 
 
 def test_all_zero_expert_routing_returns_x_times_gate_sum():
