@@ -43,8 +43,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 CALLS = {
     "moe_router_logits": ("router_logits",),
     "moe_route": ("route_topk", "route_hist"),
-    "moe_permute": ("permute_small", "permute_hist", "permute_scan_blocks",
-                    "permute_scan_experts", "permute_scatter", "permute_gather"),
+    "moe_permute": ("permute", "permute_gather"),
     "moe_expert_ffn": ("ffn_tiles", "ffn_gateup_bf16", "ffn_down_bf16", "ffn_gateup_f32",
                        "ffn_down_f32"),
     "moe_zero_experts": ("zero_experts",),
@@ -84,6 +83,11 @@ def parse():
                    help="split the fp32 router weights into their bf16 planes inside every "
                         "router call instead of once before the run (moe_router_split_weights, "
                         "a weight-format preparation outside the timed steps)")
+    p.add_argument("--companions", default="decode_bf16,skewed_bf16",
+                   help="other full-scale workloads timed after the headline on the same "
+                        "resident weights (comma-separated; 'none' to skip); each gets its own "
+                        "sub-object with ms/step, tokens/s and the expert GEMMs' HBM and MFMA "
+                        "fractions")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one plain device-to-device copy of this many MiB (the "
                         "reference dispatch that scales HBM byte counters)")
@@ -204,9 +208,28 @@ def router_similarity(w_router, reps=20):
                 gram_mfma_f32_frac=round(flops / gram_s / 1e12 / MFMA_F32_PEAK_TFLOPS, 4))
 
 
+def _host_cpu():
+    """CPU model, logical CPUs of the host and CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    return model, os.cpu_count(), allowed
+
+
 def cpu_baseline(cfg, inp, n_tokens):
-    """The oracle, single-threaded, on n_tokens sampled tokens through all six
-    stages.  Copies of expert weights to the host are not timed."""
+    """The oracle, single-threaded and pinned to one host core, on n_tokens
+    sampled tokens through all six stages, each stage timed on its own
+    (time.perf_counter, a steady clock).  Copies of expert weights to the host
+    are not timed.  Every stage's cost is linear in the tokens (rows per
+    token are fixed by the routing), so the full-batch time is extrapolated
+    per stage and labelled as such."""
     import oracle
     rng = np.random.default_rng(7)
     toks = np.sort(rng.choice(cfg.T, n_tokens, replace=False))
@@ -215,73 +238,86 @@ def cpu_baseline(cfg, inp, n_tokens):
     wr = inp["w_router"].cpu().numpy()
     b = inp["bias"].cpu().numpy()
     K, N = cfg.K, cfg.N
-    spent = 0.0
-    t0 = time.perf_counter()
-    l32 = oracle.router_logits(x, wr).astype(np.float32)
-    idx, gate, _ = oracle.route(l32, b, K)
-    off, rs, slot = oracle.permute(idx, N)
-    spent += time.perf_counter() - t0
-    xp = x[rs // K]
-    yp = np.empty((rs.size, cfg.H))
-    for e in np.nonzero(np.diff(off))[0]:
-        a, c = int(off[e]), int(off[e + 1])
-        w13e = inp["w13"][e].float().cpu().numpy()
-        w2e = inp["w2"][e].float().cpu().numpy()
+    model, ncpu, allowed = _host_cpu()
+    core = allowed[0] if allowed else None
+    if core is not None:
+        os.sched_setaffinity(0, {core})
+    stages = dict.fromkeys(("router_logits", "route", "permute", "expert_ffn", "zero_experts",
+                            "combine"), 0.0)
+    try:
         t0 = time.perf_counter()
-        yp[a:c] = oracle.ffn_rows(xp[a:c], w13e, w2e)
-        spent += time.perf_counter() - t0
-    t0 = time.perf_counter()
-    yacc = oracle.zero_experts(x, idx, gate, N)
-    oracle.combine(yp, slot, idx, gate, cfg.scale, yacc, N)
-    spent += time.perf_counter() - t0
-    return dict(value=n_tokens / spent, unit="tokens/s", cores=1, kind="oracle",
+        l32 = oracle.router_logits(x, wr).astype(np.float32)
+        t1 = time.perf_counter()
+        idx, gate, _ = oracle.route(l32, b, K)
+        t2 = time.perf_counter()
+        off, rs, slot = oracle.permute(idx, N)
+        t3 = time.perf_counter()
+        stages["router_logits"], stages["route"], stages["permute"] = t1 - t0, t2 - t1, t3 - t2
+        xp = x[rs // K]
+        yp = np.empty((rs.size, cfg.H))
+        for e in np.nonzero(np.diff(off))[0]:
+            a, c = int(off[e]), int(off[e + 1])
+            w13e = inp["w13"][e].float().cpu().numpy()
+            w2e = inp["w2"][e].float().cpu().numpy()
+            t0 = time.perf_counter()
+            yp[a:c] = oracle.ffn_rows(xp[a:c], w13e, w2e)
+            stages["expert_ffn"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        yacc = oracle.zero_experts(x, idx, gate, N)
+        t1 = time.perf_counter()
+        oracle.combine(yp, slot, idx, gate, cfg.scale, yacc, N)
+        t2 = time.perf_counter()
+        stages["zero_experts"], stages["combine"] = t1 - t0, t2 - t1
+    finally:
+        if core is not None:
+            os.sched_setaffinity(0, set(allowed))
+    spent = sum(stages.values())
+    scale = cfg.T / n_tokens
+    return dict(value=round(n_tokens / spent, 3), unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{n_tokens} of {cfg.T} tokens of {cfg.name}, all six stages, "
-                       f"single-threaded fp64 oracle ({spent:.1f} s of CPU; weight copies "
-                       f"to the host not timed)")
+                       f"single-threaded fp64 oracle pinned to one core ({spent:.1f} s of CPU; "
+                       f"weight copies to the host not timed)",
+                host_cpu_model=model, host_nproc=ncpu, pinned_core=core,
+                stage_seconds={k: round(v, 4) for k, v in stages.items()},
+                extrapolated_full_batch_seconds={
+                    "label": f"extrapolated: sample stage times x {cfg.T}/{n_tokens}",
+                    **{k: round(v * scale, 1) for k, v in stages.items()},
+                    "total": round(spent * scale, 1)})
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    cfg = workload.CONFIGS[args.workload]
-    dev = torch.device("cuda:0")
-    print(f"[bench] {cfg.name}: drawing inputs on {torch.cuda.get_device_name(dev)}",
-          file=sys.stderr, flush=True)
-    inp = workload.make_inputs(cfg, dev)
+def time_workload(cfg, inp, args, dev, x=None, bias=None, steps=None, warmup=None,
+                  profile_steps=None, log=True):
+    """Warm-up, then `steps` timed forward passes of one workload on resident
+    inputs (x / bias override the inputs of inp), then a short pass with
+    every kernel bracketed for the per-call table.  Returns a dict of the
+    timings and the buffers of the last pass."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    profile_steps = args.profile_steps if profile_steps is None else profile_steps
+    x = inp["x"] if x is None else x
+    bias = (inp["bias"] if bias is None else bias).clone()
     buf = moe.alloc_buffers(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K, cfg.torch_dtype, dev,
                             grouped_copy=args.grouped_copy,
                             separate_identity=args.separate_identity)
     if not args.router_split_per_call:
         moe.prepare_router(inp["w_router"], buf)   # once: the weights do not change
     stream = torch.cuda.current_stream(dev)
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20)
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize(dev)
-        dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        del src, dst
-
-    bias = inp["bias"].clone()
     if args.bias_controller > 0:
         integral = torch.zeros(cfg.N, dtype=torch.float32, device=dev)
         prev_err = torch.zeros(cfg.N, dtype=torch.float32, device=dev)
 
     def step():
-        moe.forward(inp["x"], inp["w_router"], bias, inp["w13"], inp["w2"], cfg.K, cfg.scale, buf)
+        moe.forward(x, inp["w_router"], bias, inp["w13"], inp["w2"], cfg.K, cfg.scale, buf)
         if args.bias_controller > 0:
             moe.moe_bias_update(buf["counts"], cfg.T, cfg.N, args.bias_controller, 1.0, 0.05, 0.2,
                                 bias, integral, prev_err)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize(dev)
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
-          file=sys.stderr, flush=True)
+    if log:
+        print(f"[bench] {cfg.name}: warmup done ({warmup} steps); timing {steps} steps",
+              file=sys.stderr, flush=True)
 
     # In the timed region only the two expert GEMM launches are bracketed by
     # HIP events (the roofline's kernel times): bracketing every launch costs
@@ -295,10 +331,10 @@ def main():
     if args.flush_mib > 0:
         scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(steps)]
     torch.cuda.synchronize(dev)
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         if args.flush_mib > 0:
             scratch.fill_(i & 0xFF)
             evs[i][0].record(stream)
@@ -309,41 +345,105 @@ def main():
     torch.cuda.synchronize(dev)
     moe.moe_profile_enable(False)
     if args.flush_mib > 0:
-        ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     else:
-        ms = start.elapsed_time(end) / args.steps
+        ms = start.elapsed_time(end) / steps
     kern_timed = moe.moe_profile_summary()
     moe.moe_profile_select(None)
 
     # the per-call table: every kernel bracketed, a few more steps
     prof_ms = None
     kern = kern_timed
-    if args.profile_steps > 0:
+    if profile_steps > 0:
         moe.moe_profile_enable(True)
         p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         p0.record(stream)
-        for _ in range(args.profile_steps):
+        for _ in range(profile_steps):
             step()
         p1.record(stream)
         torch.cuda.synchronize(dev)
         moe.moe_profile_enable(False)
         kern = moe.moe_profile_summary()
-        prof_ms = p0.elapsed_time(p1) / args.profile_steps
+        prof_ms = p0.elapsed_time(p1) / profile_steps
 
     counts = buf["counts"].cpu().numpy()
     S = int(buf["offsets"][-1].item())
     alg = algorithmic(cfg, counts, S)
-    # mean launch durations of the two expert GEMMs in the timed region
-    kname = gemm_names[0]
-    k_ms = kern_timed[gemm_names[0]][1] / kern_timed[gemm_names[0]][0]
-    d_ms = kern_timed[gemm_names[1]][1] / kern_timed[gemm_names[1]][0]
-    achieved = alg["gateup_bytes"] / (k_ms * 1e-3) / 1e9
+    gu_ms = kern_timed[gemm_names[0]][1] / kern_timed[gemm_names[0]][0]
+    dn_ms = kern_timed[gemm_names[1]][1] / kern_timed[gemm_names[1]][0]
+    return dict(ms=ms, kern_timed=kern_timed, kern=kern, prof_ms=prof_ms, counts=counts, S=S,
+                alg=alg, gemm_names=gemm_names, gu_ms=gu_ms, dn_ms=dn_ms, buf=buf,
+                steps=steps, profile_steps=profile_steps)
+
+
+def gemm_fracs(alg, gu_ms, dn_ms):
+    """HBM and MFMA fractions of the two expert GEMMs from their algorithmic
+    bytes and FLOPs and their mean launch durations."""
+    def one(nbytes, flops, ms):
+        return {"kernel_ms": round(ms, 4),
+                "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "algorithmic_bytes": int(nbytes), "gflop": round(flops / 1e9, 2)}
+    gu = one(alg["gateup_bytes"], alg["gateup_flops"], gu_ms)
+    dn = one(alg["down_bytes"], alg["down_flops"], dn_ms)
+    both_ms = gu_ms + dn_ms
+    floor_ms = max((alg["gateup_bytes"] + alg["down_bytes"]) / (HBM_PEAK_GBS * 1e9),
+                   (alg["gateup_flops"] + alg["down_flops"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    return gu, dn, {"ms": round(both_ms, 4), "floor_ms": round(floor_ms, 4),
+                    "frac_of_floor": round(floor_ms / both_ms, 4),
+                    "binding_roof": "hbm" if (alg["gateup_bytes"] + alg["down_bytes"])
+                    / (HBM_PEAK_GBS * 1e9) >= (alg["gateup_flops"] + alg["down_flops"])
+                    / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"}
+
+
+def companion(name, inp, args, dev):
+    """Another full-scale layer on the same resident expert and router
+    weights (only its tokens and bias differ): its own timed steps and the
+    same per-GEMM fractions as the headline."""
+    cfg = workload.CONFIGS[name]
+    x = workload.make_x(cfg).to(dev)
+    bias = workload.make_bias(cfg).to(dev)
+    print(f"[bench] {name}: same weights, {cfg.T} tokens", file=sys.stderr, flush=True)
+    r = time_workload(cfg, inp, args, dev, x=x, bias=bias)
+    gu, dn, ffn = gemm_fracs(r["alg"], r["gu_ms"], r["dn_ms"])
+    out = {"workload": name, "tokens": cfg.T, "ffn_scale": cfg.scale, "steps": r["steps"],
+           "ms_per_step": round(r["ms"], 4), "tokens_per_s": round(cfg.T / (r["ms"] * 1e-3), 1),
+           "gateup_gemm": gu, "down_gemm": dn, "expert_ffn": ffn,
+           "calls": call_floors(cfg, r["counts"], r["S"], r["kern"], args.grouped_copy),
+           "routing": routing_stats(cfg, r["counts"], r["S"])}
+    del r["buf"]
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    cfg = workload.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name}: drawing inputs on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    inp = workload.make_inputs(cfg, dev)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
+    r = time_workload(cfg, inp, args, dev)
+    ms, kern, alg, S, counts = r["ms"], r["kern"], r["alg"], r["S"], r["counts"]
+    gu, dn, ffn = gemm_fracs(alg, r["gu_ms"], r["dn_ms"])
+    achieved = alg["gateup_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(cfg.name),
-                    kernel=kname, kernel_ms=round(k_ms, 4),
-                    algorithmic_bytes=alg["gateup_bytes"],
-                    mfma_frac=round(alg["gateup_flops"] / (k_ms * 1e-3) / 1e12
-                                    / MFMA_BF16_PEAK_TFLOPS, 4))
+                    kernel=r["gemm_names"][0], kernel_ms=round(r["gu_ms"], 4),
+                    algorithmic_bytes=alg["gateup_bytes"], mfma_frac=gu["mfma_frac"])
+    prof_ms = r["prof_ms"]
     result = {
         "metric": METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
@@ -366,20 +466,29 @@ def main():
                    "router_weights": "split_per_call" if args.router_split_per_call
                    else "presplit_planes"},
         "roofline": roofline,
-        "down_gemm": {"kernel_ms": round(d_ms, 4),
-                      "hbm_frac": round(alg["down_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "mfma_frac": round(alg["down_flops"] / (d_ms * 1e-3) / 1e12
-                                         / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "down_gemm": {k: dn[k] for k in ("kernel_ms", "hbm_frac", "mfma_frac")},
+        "expert_ffn": ffn,
         "kernels_us": {k: round(v[1] / v[0] * 1e3, 1) for k, v in kern.items()},
         "kernels_timing": (f"expert GEMMs: HIP events in the timed region; other kernels: a "
-                           f"separate pass of {args.profile_steps} steps with every launch "
+                           f"separate pass of {r['profile_steps']} steps with every launch "
                            f"bracketed ({prof_ms:.4f} ms per step there)"
                            if prof_ms is not None else "timed region (expert GEMMs only)"),
         "calls": call_floors(cfg, counts, S, kern, args.grouped_copy),
         "routing": routing_stats(cfg, counts, S),
     }
+    del r
     if args.flush_mib > 0:
         result["cache_flush_mib_between_steps"] = args.flush_mib
+    names = [] if args.companions in ("", "none") else args.companions.split(",")
+    full_scale = all(workload.CONFIGS[n].replace(T=cfg.T, bias_mode=cfg.bias_mode,
+                                                 bias_lo=cfg.bias_lo, bias_hi=cfg.bias_hi,
+                                                 scale=cfg.scale, name=cfg.name) == cfg
+                     for n in names)
+    if names and not full_scale:
+        print("[bench] companions skipped: they need the headline's expert weights",
+              file=sys.stderr, flush=True)
+    elif names:
+        result["same_weights_workloads"] = {n: companion(n, inp, args, dev) for n in names}
     result["router_similarity"] = router_similarity(inp["w_router"])
     if args.cpu_tokens > 0:
         print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr,

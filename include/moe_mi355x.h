@@ -98,8 +98,10 @@ moe_status moe_router_logits_planes(const void *x, int x_dtype, const float *w_r
  *     expert; not renormalised over the K picks.
  *   counts[e] = number of tokens that chose e (the routing-frequency
  *     histogram), overwritten (not accumulated).
- *   dev_status (may be NULL): an int32 the kernels set to 1 when a key is NaN
- *     or a logit is not finite; they never clear it -- the caller zeroes it.
+ *   dev_status (may be NULL): an int32 the kernels set to 1 when a token's
+ *     choice or gates are undefined: a NaN key, a +inf or NaN logit, or every
+ *     logit of the token -inf (a -inf logit or key alone is a masked expert,
+ *     not an error); they never clear it -- the caller zeroes it.
  * logits [T][E], bias [E], topk_idx/topk_gate [T][K], counts [E].
  * 1 <= K <= E <= 1024, T >= 1. */
 moe_status moe_route(const float *logits, const float *bias, int T, int E, int K,
@@ -114,17 +116,19 @@ moe_status moe_route(const float *logits, const float *bias, int T, int E, int K
  *   row_src[r] = t*K + k, r < S
  *   slot_row[t*K + k] = its row, or -1 when it chose an identity expert
  * x: [T][H] (dtype); topk_idx: [T][K] with entries in [0, E) (an id outside
- * [0, n_ffn) is an identity pick: slot_row -1, no row); x_perm: capacity
- * [T*K][H]; row_src: capacity [T*K]; slot_row: [T*K]; offsets: [n_ffn + 1].
+ * [0, n_ffn) is an identity pick: slot_row -1, no row); counts: the
+ * histogram moe_route wrote for these topk_idx (entries 0..n_ffn-1 are
+ * read); x_perm: capacity [T*K][H]; row_src: capacity [T*K]; slot_row:
+ * [T*K]; offsets: [n_ffn + 1].
  * Rows >= S of x_perm and row_src are left untouched.
  * x_perm may be NULL (and then x too): only offsets, row_src and slot_row are
  * written, for moe_expert_ffn_gather, which reads the rows from x itself.
- * ws: device workspace of at least moe_permute_workspace_bytes(T, K, n_ffn). */
-size_t moe_permute_workspace_bytes(int T, int K, int n_ffn);
-moe_status moe_permute(const void *x, int dtype, const int32_t *topk_idx,
-                       int T, int H, int K, int n_ffn, int32_t *offsets,
-                       void *x_perm, int32_t *row_src, int32_t *slot_row,
-                       void *ws, size_t ws_bytes, void *stream);
+ * counts that are not the histogram of topk_idx give a meaningless grouping
+ * but no access outside the buffers (every row is clamped into [0, T*K)).
+ * No workspace: each 64-token block counts the picks it needs itself. */
+moe_status moe_permute(const void *x, int dtype, const int32_t *topk_idx, const int32_t *counts,
+                       int T, int H, int K, int n_ffn, int32_t *offsets, void *x_perm,
+                       int32_t *row_src, int32_t *slot_row, void *stream);
 
 /* The FFN experts on their grouped rows (Technical Report notes, Key claims
  * [§2.4]: fine-grained FFN experts of intermediate size I; SwiGLU form).

@@ -17,9 +17,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_MI355X_LIB selects another build of the same library (e.g. a tuning
-# variant); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_HERE, "libmoe_mi355x.so")
+# the in-tree build (python -m sparse_moe_layer_02_amd.build)
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
@@ -33,8 +32,7 @@ _SIGS = {
     "moe_router_split_weights": ([_P, _I, _I, _P, _P], _I),
     "moe_router_logits_planes": ([_P, _I, _P, _P, _I, _I, _I, _P, _P], _I),
     "moe_route": ([_P, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
-    "moe_permute_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
-    "moe_permute": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "moe_permute": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_expert_ffn_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
     "moe_expert_ffn": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_expert_ffn_gather": ([_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P,
@@ -174,24 +172,25 @@ def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
         _ptr(dev_status), _stream(logits)))
 
 
-def moe_permute_workspace_bytes(T, K, n_ffn):
-    return int(lib().moe_permute_workspace_bytes(T, K, n_ffn))
-
-
-def moe_permute(x, topk_idx, n_ffn, offsets, x_perm, row_src, slot_row, ws):
-    """Expert-major, token-ascending grouping of the FFN selections.  With
-    x_perm None only the indices are written (for moe_expert_ffn_gather); x
-    still gives T, H and the dtype."""
-    _dev(x, topk_idx, offsets, x_perm, row_src, slot_row, ws)
+def moe_permute(x, topk_idx, counts, n_ffn, offsets, x_perm, row_src, slot_row):
+    """Expert-major, token-ascending grouping of the FFN selections; counts
+    is moe_route's histogram of topk_idx.  With x_perm None only the indices
+    are written (for moe_expert_ffn_gather); x still gives T, H and the
+    dtype."""
+    _dev(x, topk_idx, counts, offsets, x_perm, row_src, slot_row)
+    for t, n in ((topk_idx, "topk_idx"), (counts, "counts"), (offsets, "offsets"),
+                 (row_src, "row_src"), (slot_row, "slot_row")):
+        _want(t, torch.int32, n)
     T, H = x.shape
     K = topk_idx.shape[1]
     assert topk_idx.shape[0] == T and row_src.numel() >= T * K and slot_row.numel() >= T * K
+    assert counts.numel() >= n_ffn and offsets.numel() >= n_ffn + 1
     if x_perm is not None:
         assert x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K
     _check("moe_permute", lib().moe_permute(
-        _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), T, H, K, n_ffn,
-        _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(topk_idx)))
+        _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), _ptr(counts),
+        T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row),
+        _stream(topk_idx)))
 
 
 def moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype):
@@ -232,18 +231,33 @@ def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
     _dev(x, topk_idx, topk_gate, y_acc)
     T, H = x.shape
     K = topk_idx.shape[1]
+    _want(topk_idx, torch.int32, "topk_idx")
+    _want(topk_gate, torch.float32, "topk_gate")
     _want(y_acc, torch.float32, "y_acc")
+    assert topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H)
     _check("moe_zero_experts", lib().moe_zero_experts(
         _ptr(x), _DT[x.dtype], _ptr(topk_idx), _ptr(topk_gate), T, H, K, n_ffn, _ptr(y_acc),
         _stream(x)))
 
 
+def _combine_args(y_perm, slot_row, topk_gate, y):
+    """Shapes and dtypes combine relies on: the C call reads y_perm rows at
+    slot_row, T*K slots and gates, [T, H] rows of its inputs."""
+    T, H = y.shape
+    K = topk_gate.shape[1]
+    _want(slot_row, torch.int32, "slot_row")
+    _want(topk_gate, torch.float32, "topk_gate")
+    assert topk_gate.shape == (T, K) and slot_row.numel() >= T * K
+    assert y_perm.dim() == 2 and y_perm.shape[1] == H and y_perm.dtype == y.dtype
+    return T, H, K
+
+
 def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
     """y = y_acc + sum of ffn_scale * gate * y_perm rows, in slot order."""
     _dev(y_perm, slot_row, topk_gate, y_acc, y)
-    T, H = y.shape
-    K = topk_gate.shape[1]
-    assert y_perm.dtype == y.dtype
+    T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
+    _want(y_acc, torch.float32, "y_acc")
+    assert y_acc.shape == (T, H)
     _check("moe_combine", lib().moe_combine(
         _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
@@ -253,11 +267,8 @@ def moe_combine_identity(y_perm, x, slot_row, topk_gate, ffn_scale, y):
     """moe_zero_experts + moe_combine in one pass: y = (sum of the identity
     slots' gates) * x + sum of ffn_scale * gate * y_perm rows, in slot order."""
     _dev(y_perm, x, slot_row, topk_gate, y)
-    T, H = y.shape
-    K = topk_gate.shape[1]
-    assert x.shape == (T, H) and y_perm.shape[1] == H and topk_gate.shape[0] == T
-    assert slot_row.numel() >= T * K
-    assert y_perm.dtype == x.dtype == y.dtype
+    T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
+    assert x.shape == (T, H) and x.dtype == y.dtype
     _check("moe_combine_identity", lib().moe_combine_identity(
         _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         T, H, K, _ptr(y), _stream(y)))
@@ -346,8 +357,6 @@ def alloc_buffers(T, H, E, n_ffn, I, K, dtype, device="cuda", grouped_copy=False
         x_perm=torch.empty((rows, H), dtype=dtype, device=device) if grouped_copy else None,
         row_src=torch.empty((rows,), dtype=i32, device=device),
         slot_row=torch.empty((rows,), dtype=i32, device=device),
-        ws_perm=torch.empty((max(16, moe_permute_workspace_bytes(T, K, n_ffn)),),
-                            dtype=torch.uint8, device=device),
         y_perm=torch.empty((rows, H), dtype=dtype, device=device),
         ws_ffn=torch.empty((max(256, moe_expert_ffn_workspace_bytes(rows, n_ffn, I, dtype)),),
                            dtype=torch.uint8, device=device),
@@ -421,13 +430,13 @@ def _dispatch_and_experts(x, K, n_ffn, w13, w2, buf):
     writes only the indices and the first expert GEMM loads each grouped row
     straight from x (0.9 GB less HBM traffic on the 8192-token layer)."""
     if buf["x_perm"] is None:
-        moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], None, buf["row_src"],
-                    buf["slot_row"], buf["ws_perm"])
+        moe_permute(x, buf["topk_idx"], buf["counts"], n_ffn, buf["offsets"], None,
+                    buf["row_src"], buf["slot_row"])
         moe_expert_ffn_gather(x, K, buf["row_src"], buf["offsets"], w13, w2, buf["y_perm"],
                               buf["ws_ffn"])
     else:
-        moe_permute(x, buf["topk_idx"], n_ffn, buf["offsets"], buf["x_perm"], buf["row_src"],
-                    buf["slot_row"], buf["ws_perm"])
+        moe_permute(x, buf["topk_idx"], buf["counts"], n_ffn, buf["offsets"], buf["x_perm"],
+                    buf["row_src"], buf["slot_row"])
         moe_expert_ffn(buf["x_perm"], buf["offsets"], w13, w2, buf["y_perm"], buf["ws_ffn"])
 
 

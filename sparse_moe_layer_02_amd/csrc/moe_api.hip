@@ -82,26 +82,20 @@ moe_status moe_route(const float* logits, const float* bias, int T, int E, int K
                                (hipStream_t)stream));
 }
 
-size_t moe_permute_workspace_bytes(int T, int K, int n_ffn) {
-  if (T < 1 || K < 1 || n_ffn < 0) return 0;
-  return permute_ws_bytes(T, K, n_ffn);
-}
-
-moe_status moe_permute(const void* x, int dtype, const int32_t* topk_idx, int T, int H, int K,
-                       int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
-                       int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
-  if ((x_perm && !x) || !topk_idx || !offsets || !row_src || !slot_row || !ws)
+moe_status moe_permute(const void* x, int dtype, const int32_t* topk_idx, const int32_t* counts,
+                       int T, int H, int K, int n_ffn, int32_t* offsets, void* x_perm,
+                       int32_t* row_src, int32_t* slot_row, void* stream) {
+  if ((x_perm && !x) || !topk_idx || !counts || !offsets || !row_src || !slot_row)
     return MOE_ERR_NULL;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
   if (T < 1 || H < 1 || H % 8 || K < 1 || n_ffn < 0 || n_ffn > kMaxFfn ||
       !fits_i32((long long)T * K))
     return MOE_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_idx, 4) || !aligned(offsets, 4) ||
-      !aligned(row_src, 4) || !aligned(slot_row, 4) || !aligned(ws, 16))
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_idx, 4) || !aligned(counts, 4) ||
+      !aligned(offsets, 4) || !aligned(row_src, 4) || !aligned(slot_row, 4))
     return MOE_ERR_ALIGN;
-  if (ws_bytes < permute_ws_bytes(T, K, n_ffn)) return MOE_ERR_WORKSPACE;
-  return launched(launch_permute(x, dtype, topk_idx, T, H, K, n_ffn, offsets, x_perm, row_src,
-                                 slot_row, ws, (hipStream_t)stream));
+  return launched(launch_permute(x, dtype, topk_idx, counts, T, H, K, n_ffn, offsets, x_perm,
+                                 row_src, slot_row, (hipStream_t)stream));
 }
 
 size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype) {

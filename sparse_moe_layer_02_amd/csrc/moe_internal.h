@@ -47,6 +47,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Order the LDS accesses of one wave across its lanes: this wave's LDS
+// writes have completed (lgkmcnt 0) and the compiler moves no memory access
+// across this point, so a lane may next read what another lane wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 inline unsigned ceil_div(size_t a, size_t b) { return (unsigned)((a + b - 1) / b); }
 
 // ---- opt-in per-kernel event timing (profile.hip) --------------------------
@@ -67,10 +77,9 @@ hipError_t launch_router_split(const float* w, int E, int H, void* planes, hipSt
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K,
                         int32_t* idx, float* gate, int32_t* counts, int32_t* status,
                         hipStream_t s);
-size_t permute_ws_bytes(int T, int K, int n_ffn);
-hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, int H, int K,
-                          int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
-                          int32_t* slot_row, void* ws, hipStream_t s);
+hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* counts,
+                          int T, int H, int K, int n_ffn, int32_t* offsets, void* x_perm,
+                          int32_t* row_src, int32_t* slot_row, hipStream_t s);
 size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype);
 // gather == nullptr: row r's activations are x_perm[r]; otherwise they are
 // token row gather[r] / gK (clamped to [0, gT)) of x_perm, i.e. of x.

@@ -2,182 +2,135 @@
 // [§2.2]: the dispatch half of dispatch/combine): every FFN selection (t, k)
 // gets a row in an expert-major buffer; inside one expert, rows follow the
 // token order.  The order must not depend on atomic arrival, so ranks are
-// computed from bitmasks:
-//   block b = tokens [64b, 64b+64), one wave; lane l is token 64b+l.
-//   mask[e] (LDS, 64 bits) = OR of (1 << l) over the lanes that chose e.
-//   A token chooses an expert at most once, so
-//     rank of (t, e) inside block b = popcount(mask[e] & lanes below l),
-//     cnt[e][b]                      = popcount(mask[e]).
-//   row(t, e) = offsets[e] + sum_{b' < b} cnt[e][b'] + rank.
-// Kernels: hist (cnt), scan over blocks per expert, scan over experts
-// (offsets), scatter (slot_row, row_src), and, when a grouped copy is asked
-// for, gather (x rows, one read of x[t] feeding all of its rows).
+// computed from bitmasks, in one kernel:
+//   block b = tokens [64b, 64b+64) (1024 threads).
+//   mask[e] (LDS, 64 bits) = OR of (1 << (t - 64b)) over its tokens t that
+//     chose e.  A token chooses an expert at most once, so the rank of (t, e)
+//     among the block's rows of e is popcount(mask[e] & bits below t - 64b).
+//   before[e] = picks of e by tokens < 64b.  The block counts them itself
+//     (an LDS histogram of the picks on the shorter side of its tokens: those
+//     before it, or those after it, whence before[e] = counts[e] - after[e]
+//     - popcount(mask[e])), so no other block's result is awaited and there
+//     is no second launch.  Each block reads at most half of the T*K picks.
+//   offsets = exclusive scan of counts over the FFN experts (every block
+//     scans the n_ffn counts; block 0 writes them).
+//   row(t, e) = offsets[e] + before[e] + rank.
+// When a grouped copy is asked for, perm_gather then copies the x rows (one
+// read of x[t] feeding all of its rows).
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kBlockTokens = 64;
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;
 
-// LDS mask table of one wave: one 64-bit word per FFN expert.
-__device__ __forceinline__ void build_masks(unsigned long long* mask, const int32_t* idx, int T,
-                                            int K, int n_ffn, int blk) {
-  const int lane = threadIdx.x;
-  for (int e = lane; e < n_ffn; e += kWave) mask[e] = 0ull;
-  __syncthreads();
-  const int t = blk * kBlockTokens + lane;
-  if (t < T) {
-    const int32_t* row = idx + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-      int e = row[k];
-      if ((unsigned)e < (unsigned)n_ffn) atomicOr(&mask[e], 1ull << lane);
-    }
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kWave) void perm_hist(const int32_t* __restrict__ idx, int T, int K,
-                                                   int n_ffn, int nblk,
-                                                   int32_t* __restrict__ cnt) {
-  extern __shared__ unsigned long long mask[];
-  const int blk = blockIdx.x;
-  build_masks(mask, idx, T, K, n_ffn, blk);
-  for (int e = threadIdx.x; e < n_ffn; e += kWave)
-    cnt[(size_t)e * nblk + blk] = __popcll(mask[e]);
-}
-
-// One wave per expert: exclusive scan of cnt[e][0..nblk) in place; tot[e].
-__global__ __launch_bounds__(256) void perm_scan_blocks(int32_t* __restrict__ cnt, int nblk,
-                                                        int n_ffn, int32_t* __restrict__ tot) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (e >= n_ffn) return;
-  int32_t* row = cnt + (size_t)e * nblk;
-  int carry = 0;
-  for (int base = 0; base < nblk; base += kWave) {
-    const int b = base + lane;
-    const int v = b < nblk ? row[b] : 0;
-    int incl = v;
+// Exclusive scan of v over the block's 1024 threads (fixed order); *total
+// receives the sum.  Uses part[kPermWaves + 1] of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* part, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int incl = v;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (b < nblk) row[b] = carry + incl - v;
-    carry += __shfl(incl, kWave - 1);
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  if (lane == 0) tot[e] = carry;
+  if (lane == kWave - 1) part[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int x = part[w];
+      part[w] = run;
+      run += x;
+    }
+    part[kPermWaves] = run;
+  }
+  __syncthreads();
+  *total = part[kPermWaves];
+  return part[wave] + incl - v;
 }
 
-// One block: offsets = exclusive scan of tot over experts, offsets[n] = total.
-__global__ __launch_bounds__(1024) void perm_scan_experts(const int32_t* __restrict__ tot,
-                                                          int n_ffn,
-                                                          int32_t* __restrict__ offsets) {
-  __shared__ int part[1024];
+__global__ __launch_bounds__(kPermThreads) void perm_fused(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts, int T, int K, int n_ffn,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_src,
+    int32_t* __restrict__ slot_row) {
+  extern __shared__ unsigned long long mask[];        // [n_ffn]
+  int* before = (int*)(mask + n_ffn);                  // [n_ffn]: side counts, then row bases
+  __shared__ int part[kPermWaves + 1];
   const int tid = threadIdx.x;
-  const int per = (n_ffn + 1023) / 1024;
-  const int lo = min(n_ffn, tid * per), hi = min(n_ffn, lo + per);
-  int s = 0;
-  for (int e = lo; e < hi; ++e) s += tot[e];
-  part[tid] = s;
+  const int t0 = blockIdx.x * kBlockTokens, t1 = min(T, t0 + kBlockTokens);
+  for (int e = tid; e < n_ffn; e += kPermThreads) {
+    mask[e] = 0ull;
+    before[e] = 0;
+  }
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // the block's own picks
+  const int p0 = t0 * K, p1 = t1 * K;
+  for (int i = p0 + tid; i < p1; i += kPermThreads) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)n_ffn) atomicOr(&mask[e], 1ull << (i / K - t0));
   }
-  int run = part[tid] - s;  // exclusive prefix of this thread's chunk
-  for (int e = lo; e < hi; ++e) {
-    offsets[e] = run;
-    run += tot[e];
-  }
-  if (tid == 1023) offsets[n_ffn] = part[1023];
-}
-
-__global__ __launch_bounds__(kWave) void perm_scatter(const int32_t* __restrict__ idx, int T,
-                                                      int K, int n_ffn, int nblk,
-                                                      const int32_t* __restrict__ pre,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ row_src,
-                                                      int32_t* __restrict__ slot_row) {
-  extern __shared__ unsigned long long mask[];
-  const int blk = blockIdx.x;
-  build_masks(mask, idx, T, K, n_ffn, blk);
-  const int lane = threadIdx.x;
-  const int t = blk * kBlockTokens + lane;
-  if (t >= T) return;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int k = 0; k < K; ++k) {
-    const int s = t * K + k;
-    const int e = idx[s];
-    if ((unsigned)e < (unsigned)n_ffn) {   // other ids: not an FFN pick
-      const int row = offsets[e] + pre[(size_t)e * nblk + blk] + __popcll(mask[e] & below);
-      slot_row[s] = row;
-      row_src[row] = s;
-    } else {
-      slot_row[s] = -1;
+  // the picks on the shorter side
+  const bool lower = t0 <= T - t1;
+  const int s0 = lower ? 0 : p1, s1 = lower ? p0 : T * K;
+  auto count = [&](int e) {
+    if ((unsigned)e < (unsigned)n_ffn) atomicAdd(&before[e], 1);
+  };
+  int s_vec = s0;
+  if ((((uintptr_t)idx) & 15) == 0 && (s0 & 3) == 0) {
+    // 16-byte loads, four in flight per thread
+    const i32x4* v4 = (const i32x4*)idx;
+    const int q0 = s0 >> 2, q1 = s1 >> 2;
+    int q = q0 + tid;
+    for (; q + 3 * kPermThreads < q1; q += 4 * kPermThreads) {
+      i32x4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = v4[q + u * kPermThreads];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) count(a[u][j]);
     }
-  }
-}
-
-// T <= 64 (decode): the tokens are one 64-token block, so the histogram,
-// both scans and the scatter fit one workgroup -- one launch instead of four
-// (the four cost ~27 us at 64 tokens, almost all launch latency).  Wave 0
-// (lane = token) builds the masks and scatters; all 1024 threads scan the
-// experts.  The rows are those of the general path: offsets[e] +
-// popcount(mask[e] & lanes below).  LDS: n_ffn masks, then n_ffn offsets.
-__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ idx, int T, int K,
-                                                   int n_ffn, int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ row_src,
-                                                   int32_t* __restrict__ slot_row) {
-  extern __shared__ unsigned long long mask[];
-  int* off = (int*)(mask + n_ffn);
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < n_ffn; e += 1024) mask[e] = 0ull;
-  __syncthreads();
-  if (tid < kWave && tid < T) {
-    const int32_t* row = idx + (size_t)tid * K;
-    for (int k = 0; k < K; ++k) {
-      const int e = row[k];
-      if ((unsigned)e < (unsigned)n_ffn) atomicOr(&mask[e], 1ull << tid);
+    for (; q < q1; q += kPermThreads) {
+      const i32x4 a = v4[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) count(a[j]);
     }
+    s_vec = q1 << 2;
   }
+  for (int i = s_vec + tid; i < s1; i += kPermThreads) count(idx[i]);
   __syncthreads();
-  // exclusive scan of the per-expert counts: a chunk of experts per thread
-  const int per = (n_ffn + 1023) / 1024;
+  // offsets (a chunk of experts per thread) and the block's row bases
+  const int per = (n_ffn + kPermThreads - 1) / kPermThreads;
   const int lo = min(n_ffn, tid * per), hi = min(n_ffn, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; ++e) sum += __popcll(mask[e]);
-  part[tid] = sum;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
+  for (int e = lo; e < hi; ++e) sum += counts[e];
+  int total;
+  int run = block_exclusive_scan(sum, part, &total);
   for (int e = lo; e < hi; ++e) {
-    off[e] = run;
-    offsets[e] = run;
-    run += __popcll(mask[e]);
+    const int c = counts[e];
+    if (blockIdx.x == 0) offsets[e] = run;
+    before[e] = run + (lower ? before[e] : c - before[e] - __popcll(mask[e]));
+    run += c;
   }
-  if (tid == 1023) offsets[n_ffn] = part[1023];
+  if (blockIdx.x == 0 && tid == 0) offsets[n_ffn] = total;
   __syncthreads();
-  if (tid < kWave && tid < T) {
-    const unsigned long long below = (1ull << tid) - 1ull;
-    for (int k = 0; k < K; ++k) {
-      const int s = tid * K + k;
-      const int e = idx[s];
-      if ((unsigned)e < (unsigned)n_ffn) {
-        const int r = off[e] + __popcll(mask[e] & below);
-        slot_row[s] = r;
-        row_src[r] = s;
-      } else {
-        slot_row[s] = -1;
-      }
+  // rows of the block's picks.  With counts as moe_route wrote them for idx,
+  // every row is in [0, T*K); otherwise rows are clamped into that range, so
+  // no write leaves the buffers (the grouping is then meaningless).
+  const int cap = T * K;
+  for (int i = p0 + tid; i < p1; i += kPermThreads) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)n_ffn) {
+      const int l = i / K - t0;
+      int row = before[e] + __popcll(mask[e] & ((1ull << l) - 1ull));
+      row = min(max(row, 0), cap - 1);
+      slot_row[i] = row;
+      row_src[row] = i;
+    } else {
+      slot_row[i] = -1;   // an identity pick: no row
     }
   }
 }
@@ -223,40 +176,16 @@ __global__ __launch_bounds__(256) void perm_gather_long(const i32x4* __restrict_
   }
 }
 
-inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-
 }  // namespace
 
-size_t permute_ws_bytes(int T, int K, int n_ffn) {
-  (void)K;
-  const size_t nblk = (size_t)(T + kBlockTokens - 1) / kBlockTokens;
-  return align256((size_t)n_ffn * nblk * 4) + align256((size_t)n_ffn * 4 + 4);
-}
-
-hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, int T, int H, int K,
-                          int n_ffn, int32_t* offsets, void* x_perm, int32_t* row_src,
-                          int32_t* slot_row, void* ws, hipStream_t s) {
-  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
-  int32_t* cnt = (int32_t*)ws;
-  int32_t* tot = (int32_t*)((char*)ws + align256((size_t)n_ffn * nblk * 4));
-  const size_t lds = (size_t)(n_ffn > 0 ? n_ffn : 1) * sizeof(unsigned long long);
-  if (nblk == 1 && n_ffn > 0) {
-    MOE_LAUNCH("permute_small", s,
-               perm_small<<<1, 1024, (size_t)n_ffn * 12, s>>>(idx, T, K, n_ffn, offsets, row_src,
-                                                              slot_row));
-  } else {
-    if (n_ffn > 0) {
-      MOE_LAUNCH("permute_hist", s,
-                 perm_hist<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt));
-      MOE_LAUNCH("permute_scan_blocks", s,
-                 perm_scan_blocks<<<ceil_div(n_ffn, 4), 256, 0, s>>>(cnt, nblk, n_ffn, tot));
-    }
-    MOE_LAUNCH("permute_scan_experts", s,
-               perm_scan_experts<<<1, 1024, 0, s>>>(tot, n_ffn, offsets));
-    MOE_LAUNCH("permute_scatter", s,
-               perm_scatter<<<nblk, kWave, lds, s>>>(idx, T, K, n_ffn, nblk, cnt, offsets,
-                                                     row_src, slot_row));
-  }
+hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* counts,
+                          int T, int H, int K, int n_ffn, int32_t* offsets, void* x_perm,
+                          int32_t* row_src, int32_t* slot_row, hipStream_t s) {
+  const unsigned nblk = ceil_div(T, kBlockTokens);
+  const size_t lds = (size_t)(n_ffn > 0 ? n_ffn : 1) * 12;
+  MOE_LAUNCH("permute", s,
+             perm_fused<<<nblk, kPermThreads, lds, s>>>(idx, counts, T, K, n_ffn, offsets,
+                                                         row_src, slot_row));
   if (!x_perm) return hipGetLastError();   // indices only: the GEMM gathers x rows itself
   const int esize = dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = (int)((size_t)H * esize / 16);

@@ -4,16 +4,14 @@
 // unbiased logits at the picks; counts is the routing-frequency histogram.
 //
 // One wave64 per token.  Lane l holds experts e = l + 64*i (i < EPL).  Each
-// candidate is one 64-bit integer whose unsigned order is the selection order
-// (a lane keeps only the high words and forms the integer of its best):
-//   high 32 bits: the fp32 key mapped to an order-preserving integer
-//                 (-0.0 folded onto +0.0; NaN below -inf),
-//   low 32 bits : ~e, so that on equal keys the lower expert id is larger.
-// Zero marks a taken (or absent) candidate.  K rounds of a lane-local max and
-// a wave max yield the picks in order.  Wave reductions use DPP row shifts
-// and row broadcasts (the result lands in lane 63 and is read out once)
-// rather than LDS-routed shuffles: the K rounds are a serial chain per token,
-// so the latency of each step is what the kernel pays.
+// key becomes a 32-bit word whose unsigned order is the key order (-0.0
+// folded onto +0.0, NaN below -inf, 0 = absent), and a candidate is the
+// 64-bit integer (key word, ~e), so that on equal keys the lower expert id is
+// larger.  The K largest candidates are found by a threshold and a rank
+// among the few candidates above it (select_token); K rounds of a wave max
+// over every candidate remain for the cases the threshold cannot narrow.
+// Wave reductions use DPP row shifts and row broadcasts (the result lands in
+// lane 63 and is read out once) rather than LDS-routed shuffles.
 // counts comes from a second kernel over the picks (route_hist), so that the
 // top-K kernel's 4-token blocks do not each add a histogram to counts with
 // global atomics (on a 96-expert pool that contention cost more than the
@@ -119,6 +117,133 @@ __global__ __launch_bounds__(kHistThreads) void route_hist(const int32_t* __rest
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111>(v, 0u));         // row_shr:1
+  v = max(v, dpp_u32<0x112>(v, 0u));         // row_shr:2
+  v = max(v, dpp_u32<0x114>(v, 0u));         // row_shr:4
+  v = max(v, dpp_u32<0x118>(v, 0u));         // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xa>(v, 0u));    // row_bcast:15
+  v = max(v, dpp_u32<0x143, 0xc>(v, 0u));    // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Lanes below this one holding a set bit of `bits` (a ballot).
+__device__ __forceinline__ int lanes_below(uint64_t bits) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+}
+
+// Selection of one token's K picks (one wave; lane l holds the key words
+// kq[i] and logits lg[i] of experts l + 64 i).
+//
+// Fast path (K <= 64).  The K-th largest of the 64 lane maxima, theta, is a
+// lower bound of the K-th largest key (the K largest lane maxima are K
+// distinct keys >= theta), so every key of the top K -- ties at the K-th
+// key included -- is >= theta.  theta comes from at most K rounds of a
+// 32-bit wave max over one value per lane.  The candidates (keys >= theta,
+// usually K plus a few) are compacted into LDS, and each is ranked by
+// comparing its 64-bit (key word, ~e) against all of them: rank r < K is
+// pick r.  The order is the rounds' order exactly (descending key, lower id
+// first on equal keys), in a few hundred vector instructions per token
+// instead of K rounds over every key.  More than 64 candidates (many keys
+// equal at theta) take the rounds below.
+template <int EPL>
+__device__ __forceinline__ void select_token(const uint32_t (&kq0)[EPL], const float (&lg)[EPL],
+                                             int E, int K, float mx, float den, int lane,
+                                             uint64_t* cand, float* cand_lg, float* lrow,
+                                             int32_t* __restrict__ idx_row,
+                                             float* __restrict__ gate_row) {
+  uint32_t kq[EPL];
+  uint32_t lm = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    kq[i] = kq0[i];
+    lm = max(lm, kq[i]);
+  }
+  if (K <= kWave) {
+    // theta: the K-th largest lane maximum, counted with multiplicity.  At
+    // least K lanes hold a key (K <= E and K <= 64), and every key word is
+    // >= 1, so each round removes at least one lane and ends by round K.
+    uint32_t theta = 1, v = lm;
+    int seen = 0;
+    for (int r = 0; r < K; ++r) {
+      const uint32_t w = wave_max_u32(v);
+      const uint64_t hit = __ballot(v == w);
+      seen += __popcll(hit);
+      theta = w;
+      if (seen >= K) break;
+      if (v == w) v = 0;
+    }
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) c += kq[i] >= theta ? 1 : 0;
+    // exclusive prefix of c over the lanes (c <= 16: five bit planes)
+    int pre = 0, M = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+      const uint64_t bits = __ballot((c >> b) & 1);
+      pre += lanes_below(bits) << b;
+      M += __popcll(bits) << b;
+    }
+    if (M <= kWave) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (kq[i] >= theta) {
+          cand[pre] = ((uint64_t)kq[i] << 32) | (uint32_t)(~(uint32_t)(lane + kWave * i));
+          cand_lg[pre] = lg[i];
+          ++pre;
+        }
+      wave_lds_sync();   // the wave's writes land before a lane reads another's
+      if (lane < M) {
+        const uint64_t mine = cand[lane];
+        int rank = 0;
+        for (int m = 0; m < M; ++m) rank += cand[m] > mine ? 1 : 0;
+        if (rank < K) {
+          idx_row[rank] = (int)(~(uint32_t)mine);
+          gate_row[rank] = expf(cand_lg[lane] - mx) / den;
+        }
+      }
+      wave_lds_sync();   // cand is rewritten for the wave's next token
+      return;
+    }
+  }
+  // Rounds: K times, the largest remaining 64-bit candidate of the wave.
+  // The token's logits go to LDS for the gates; pick k stays in lane k % 64,
+  // and every 64 picks (or at the last) the lanes write them at once.
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + kWave * i < E) lrow[lane + kWave * i] = lg[i];
+  wave_lds_sync();
+  int pick = 0;
+  for (int k = 0; k < K; ++k) {
+    // the lane's best: the largest key word, the lowest i among equal ones
+    uint32_t bk = 0;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (kq[i] > bk) {
+        bk = kq[i];
+        bi = i;
+      }
+    const uint64_t mine =
+        bk ? ((uint64_t)bk << 32) | (uint32_t)(~(uint32_t)(lane + kWave * bi)) : 0ull;
+    const uint64_t best = wave_max_u64(mine);
+    const int e = (int)(~(uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i == e) kq[i] = 0;
+    if (lane == (k & (kWave - 1))) pick = e;
+    if ((k & (kWave - 1)) == kWave - 1 || k == K - 1) {
+      const int base = k & ~(kWave - 1);
+      if (lane <= k - base) {
+        idx_row[base + lane] = pick;
+        gate_row[base + lane] = expf(lrow[pick] - mx) / den;
+      }
+    }
+  }
+  wave_lds_sync();
+}
+
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int K,
@@ -129,69 +254,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   constexpr int kWaves = kRouteThreads / kWave;
-  // the token's logits, for the softmax sum and the gates of its picks: kept
-  // in LDS rather than in registers through the K rounds (94 -> 73 VGPRs at
-  // 12 logits per lane, one more wave per SIMD)
-  __shared__ float lrow[kWaves][kWave * EPL];
+  __shared__ uint64_t cand[kWaves][kWave];
+  __shared__ float cand_lg[kWaves][kWave];
+  __shared__ float lrow[kWaves][kWave * EPL];   // the rounds' gates
   bool bad = false;
   const int t_end = min(T, (blockIdx.x + 1) * kTokensPerBlock);
   for (int t = blockIdx.x * kTokensPerBlock + wave; t < t_end; t += kWaves) {
     const float* lr = logits + (size_t)t * E;
-    // the candidates' key words; the low word ~e of candidate i follows
-    // from lane and i, so it is formed only for the lane's best
     uint32_t kq[EPL];
+    float lg[EPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      int e = lane + kWave * i;
+      const int e = lane + kWave * i;
       if (e < E) {
-        const float lg = lr[e];
-        lrow[wave][e] = lg;
-        float key = lg + bias[e];
-        bad |= (key != key) || !isfinite(lg);
+        lg[i] = lr[e];
+        const float key = lg[i] + bias[e];
+        // -inf (a masked expert) is a valid key and logit; a NaN key or a
+        // +inf logit leaves the selection or the softmax undefined
+        bad |= (key != key) || (lg[i] == INFINITY);
         kq[i] = key_order(key);
-        mx = fmaxf(mx, lg);
+        mx = fmaxf(mx, lg[i]);
       } else {
+        lg[i] = -INFINITY;
         kq[i] = 0;
       }
     }
     // softmax statistics over the unbiased logits (fixed reduction order)
     mx = wave_max_f32(mx);
+    bad |= mx == -INFINITY;   // every logit -inf: no softmax
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) part += expf(lrow[wave][lane + kWave * i] - mx);
+      if (lane + kWave * i < E) part += expf(lg[i] - mx);
     const float den = wave_sum_f32(part);
-
-    // the rounds only select: pick k is kept in lane k % 64, and every 64
-    // picks (or at the last) the lanes write them and their gates at once
-    int pick = 0;
-    for (int k = 0; k < K; ++k) {
-      // the lane's best: the largest key word, the lowest i among equal ones
-      uint32_t bk = 0;
-      int bi = 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (kq[i] > bk) {
-          bk = kq[i];
-          bi = i;
-        }
-      const uint64_t mine =
-          bk ? ((uint64_t)bk << 32) | (uint32_t)(~(uint32_t)(lane + kWave * bi)) : 0ull;
-      const uint64_t best = wave_max_u64(mine);
-      const int e = (int)(~(uint32_t)best);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i == e) kq[i] = 0;
-      if (lane == (k & (kWave - 1))) pick = e;
-      if ((k & (kWave - 1)) == kWave - 1 || k == K - 1) {
-        const int base = k & ~(kWave - 1);
-        if (lane <= k - base) {
-          idx[(size_t)t * K + base + lane] = pick;
-          gate[(size_t)t * K + base + lane] = expf(lrow[wave][pick] - mx) / den;
-        }
-      }
-    }
+    select_token<EPL>(kq, lg, E, K, mx, den, lane, cand[wave], cand_lg[wave], lrow[wave],
+                      idx + (size_t)t * K, gate + (size_t)t * K);
   }
   if (bad && status) *status = 1;
 }

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import sparse_moe_layer_02_amd as moe
 
@@ -25,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -40,8 +41,6 @@ def test_status_strings():
 
 def test_workspace_queries():
     lib = moe.lib()
-    assert lib.moe_permute_workspace_bytes(8192, 12, 512) >= 512 * 128 * 4
-    assert lib.moe_permute_workspace_bytes(0, 12, 512) == 0
     # the FFN workspace holds the intermediate activations: rows x I elements
     b16 = lib.moe_expert_ffn_workspace_bytes(98304, 512, 2048, 1)
     f32 = lib.moe_expert_ffn_workspace_bytes(98304, 512, 2048, 0)
@@ -94,25 +93,26 @@ def test_route_validation():
 
 def test_permute_validation():
     f = moe.lib().moe_permute
-    need = moe.lib().moe_permute_workspace_bytes(64, 4, 16)
-    args = [FAKE, 1, FAKE, 64, 256, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, need, None]
-    a = list(args); a[11] = None
+    args = [FAKE, 1, FAKE, FAKE, 64, 256, 4, 16, FAKE, FAKE, FAKE, FAKE, None]
+    a = list(args); a[3] = None                   # counts are required
     assert f(*a) == NULL
-    a = list(args); a[4] = 250                    # H not a multiple of 8
+    a = list(args); a[5] = 250                    # H not a multiple of 8
     assert f(*a) == SHAPE
-    a = list(args); a[6] = 5000                   # too many FFN experts
+    a = list(args); a[7] = 5000                   # too many FFN experts
     assert f(*a) == SHAPE
-    a = list(args); a[12] = need - 1
-    assert f(*a) == WS
-    a = list(args); a[8] = P(0x10008)             # x_perm not 16-byte aligned
+    a = list(args); a[9] = P(0x10008)             # x_perm not 16-byte aligned
+    assert f(*a) == ALIGN
+    a = list(args); a[3] = P(0x10002)             # counts not 4-byte aligned
     assert f(*a) == ALIGN
     a = list(args); a[0] = None                   # x without x_perm to copy into
     assert f(*a) == NULL
-    a = list(args); a[0] = None; a[8] = None      # indices only (no copy): x unused
-    a[6] = 5000
+    a = list(args); a[0] = None; a[9] = None      # indices only (no copy): x unused
+    a[7] = 5000
     assert f(*a) == SHAPE                         # still validated past the NULL check
-    a = list(args); a[9] = None                   # row_src is always written
+    a = list(args); a[10] = None                  # row_src is always written
     assert f(*a) == NULL
+    a = list(args); a[4] = 1 << 28; a[6] = 16     # T*K >= 2^31
+    assert f(*a) == SHAPE
 
 
 def test_expert_ffn_validation():
@@ -248,4 +248,4 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
     with pytest.raises(RuntimeError, match="missing"):
-        moe.moe_permute_workspace_bytes(64, 12, 512)
+        moe.moe_expert_ffn_workspace_bytes(64, 12, 512, torch.bfloat16)

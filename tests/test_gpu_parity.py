@@ -202,6 +202,82 @@ def test_route_flags_nan_keys():
     assert int(host(status)[0]) == 1
 
 
+def _route(l, b, K, status=None):
+    dev = device()
+    T, E = l.shape
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev) if status is None else status
+    moe.moe_route(torch.from_numpy(l).to(dev), torch.from_numpy(b).to(dev), K, idx, gate, counts,
+                  status)
+    torch.cuda.synchronize()
+    return host(idx), host(gate), host(counts), int(host(status)[0])
+
+
+def test_route_minus_inf_logits_are_masked_experts():
+    # A -inf logit (or key) is a masked expert, not an error: it is never
+    # picked before a finite key, and its gate is 0 when K exceeds the
+    # unmasked experts.  Full pool (768 experts, K = 12), both selection
+    # paths: a token with 5 finite logits takes masked experts by lowest id.
+    rng = np.random.default_rng(21)
+    T, E, K = 150, 768, 12
+    l = (rng.standard_normal((T, E)) * 0.5).astype(np.float32)
+    l[rng.random((T, E)) < 0.3] = -np.inf
+    l[7] = -np.inf
+    l[7, [3, 100, 400, 700, 767]] = [0.1, -0.2, 0.3, 0.0, 1.0]
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    idx, gate, counts, status = _route(l, b, K)
+    i_ref, g_ref, c_ref = oracle.route(l, b, K)
+    np.testing.assert_array_equal(idx, i_ref)
+    np.testing.assert_array_equal(counts, c_ref)
+    assert normwise(gate, g_ref) <= 1e-6
+    assert (gate[7, 5:] == 0).all() and status == 0
+
+
+def test_route_flags_undefined_softmax():
+    # +inf logit, NaN logit, or every logit -inf: the gates are undefined
+    for case in ("+inf", "nan", "all -inf"):
+        l = np.zeros((4, 24), np.float32)
+        if case == "+inf":
+            l[1, 3] = np.inf
+        elif case == "nan":
+            l[2, 5] = np.nan
+        else:
+            l[3, :] = -np.inf
+        _, _, _, status = _route(l, np.zeros(24, np.float32), 4)
+        assert status == 1, case
+    # -inf on some experts only, and a -inf bias: no flag
+    l = np.zeros((4, 24), np.float32)
+    l[0, :20] = -np.inf
+    b = np.zeros(24, np.float32)
+    b[21] = -np.inf
+    _, _, _, status = _route(l, b, 4)
+    assert status == 0
+
+
+def test_permute_rows_stay_in_bounds_with_inconsistent_counts():
+    # counts that are not the histogram of topk_idx give a meaningless
+    # grouping, but every row written stays inside [0, T*K)
+    dev = device()
+    T, E, N, K = 300, 96, 64, 8
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    it = torch.from_numpy(idx).to(dev)
+    x = torch.zeros((T, 256), dtype=torch.bfloat16, device=dev)
+    for bad in (np.zeros(E, np.int32), np.full(E, 1 << 20, np.int32)):
+        offsets = torch.empty(N + 1, dtype=torch.int32, device=dev)
+        row_src = torch.full((T * K + 64,), -7, dtype=torch.int32, device=dev)
+        slot_row = torch.empty(T * K, dtype=torch.int32, device=dev)
+        moe.moe_permute(x, it, torch.from_numpy(bad).to(dev), N, offsets, None, row_src,
+                        slot_row)
+        torch.cuda.synchronize()
+        sr = host(slot_row)
+        assert ((sr == -1) | ((sr >= 0) & (sr < T * K))).all()
+        assert (sr == -1).sum() == (idx >= N).sum()
+        assert (host(row_src)[T * K:] == -7).all()
+
+
 def test_forward_is_bitwise_deterministic():
     cfg = workload.CONFIGS["mid_bf16"].replace(T=1024)
     inp, buf = _run(cfg)
