@@ -49,7 +49,8 @@ typedef enum {
     MOE_ERR_DTYPE = 3,     /* unknown dtype */
     MOE_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
     MOE_ERR_WORKSPACE = 5, /* workspace smaller than the *_workspace_bytes query */
-    MOE_ERR_LAUNCH = 6     /* a HIP launch failed (hipGetLastError) */
+    MOE_ERR_LAUNCH = 6,    /* a HIP launch failed (hipGetLastError) */
+    MOE_ERR_TOO_LARGE = 7  /* the sizes need more than a fixed scratch holds */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -164,6 +165,29 @@ moe_status moe_expert_ffn_gather(const void *x, int T, int K, const int32_t *row
                                  const int32_t *offsets, int rows_cap, int n_ffn, int H,
                                  int I, const void *w13, const void *w2, int dtype,
                                  void *y_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_expert_ffn_gather for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels, with the workspace (the m-tile list and the
+ * bf16 hh rows between the two GEMMs) taken from a fixed scratch array that
+ * the library holds on every GPU it runs on until the process ends, instead
+ * of a caller-allocated ws.  Nothing is allocated by the call.
+ *   Limit: moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype) must
+ *   not exceed MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES (32 MiB: e.g. rows_cap
+ *   up to ~8,000 FFN rows at I = 2048, i.e. decode-sized batches), else
+ *   MOE_ERR_TOO_LARGE and nothing is enqueued.
+ *   Every call on one GPU uses that GPU's one scratch array: calls that
+ *   overlap on one GPU (other streams, other threads) race and must be
+ *   ordered, e.g. on one stream.  The scratch needs no clearing: each call
+ *   writes the parts it reads.  The first call on a device looks up the
+ *   array's address there (a runtime query, not an allocation).
+ * Arguments, results (bit for bit those of moe_expert_ffn_gather) and the
+ * other errors as for moe_expert_ffn_gather, without ws and ws_bytes. */
+#define MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status moe_expert_ffn_gather_noalloc(const void *x, int T, int K, const int32_t *row_src,
+                                         const int32_t *offsets, int rows_cap, int n_ffn, int H,
+                                         int I, const void *w13, const void *w2, int dtype,
+                                         void *y_perm, void *stream);
 
 /* Zero-computation experts (Technical Report notes, Key claims [§2.1]:
  * identity experts return their input):

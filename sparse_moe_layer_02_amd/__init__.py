@@ -37,6 +37,8 @@ _SIGS = {
     "moe_expert_ffn": ([_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "moe_expert_ffn_gather": ([_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P,
                                ctypes.c_size_t, _P], _I),
+    "moe_expert_ffn_gather_noalloc": ([_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P],
+                                      _I),
     "moe_zero_experts": ([_P, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_P, _I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P], _I),
     "moe_combine_identity": ([_P, _P, _I, _P, _P, ctypes.c_float, _I, _I, _I, _P, _P], _I),
@@ -224,6 +226,27 @@ def moe_expert_ffn_gather(x, K, row_src, offsets, w13, w2, y_perm, ws):
     _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
         _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
         _DT[x.dtype], _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES
+
+
+def moe_expert_ffn_gather_noalloc(x, K, row_src, offsets, w13, w2, y_perm):
+    """moe_expert_ffn_gather with its workspace in the library's fixed
+    per-GPU scratch (no allocation; for callers that cannot allocate).
+    Calls that overlap on one GPU race; order them on one stream."""
+    _dev(x, row_src, offsets, w13, w2, y_perm)
+    _want(row_src, torch.int32, "row_src")
+    T, H = x.shape
+    rows_cap = y_perm.shape[0]
+    N, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H
+    assert row_src.numel() >= rows_cap
+    assert w13.dtype == w2.dtype == x.dtype == y_perm.dtype
+    _check("moe_expert_ffn_gather_noalloc", lib().moe_expert_ffn_gather_noalloc(
+        _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
+        _DT[x.dtype], _ptr(y_perm), _stream(x)))
 
 
 def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):

@@ -39,6 +39,8 @@
 //     the m-tile's activation rows from that XCD's L2; the column tiles start
 //     their K sweeps at a few different offsets, so that those re-reads are L2
 //     hits rather than 32 simultaneous waits on one miss.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -642,6 +644,34 @@ inline int ffn_bm(int dtype) { return dtype == MOE_BF16 ? kBmBf16 : kBmF32; }
 inline size_t max_mtiles(int rows_cap, int n_ffn, int bm) { return (size_t)rows_cap / bm + n_ffn + 8; }
 
 }  // namespace
+
+// The workspace of moe_expert_ffn_gather_noalloc: one fixed array per GPU,
+// alive until the process ends.  Host code never uses the name `scratch`
+// (a host-side stand-in); it uses the device address looked up once per
+// device with that device current.
+static __device__ __align__(256) char scratch[MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;

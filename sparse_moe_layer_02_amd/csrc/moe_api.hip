@@ -31,6 +31,7 @@ const char* moe_status_string(int s) {
     case MOE_ERR_ALIGN: return "misaligned pointer";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_TOO_LARGE: return "sizes exceed the fixed scratch";
     default: return "unknown status";
   }
 }
@@ -104,11 +105,12 @@ size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype)
 }
 
 namespace {
-// The checks both expert-FFN entry points share; a is the activation source.
+// The checks the expert-FFN entry points share; a is the activation source.
+// check_ws = false: the workspace is the library's own (noalloc variant).
 moe_status ffn_checks(const void* a, const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
                       const void* w13, const void* w2, int dtype, const void* y_perm,
-                      const void* ws, size_t ws_bytes) {
-  if (!a || !offsets || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_NULL;
+                      const void* ws, size_t ws_bytes, bool check_ws = true) {
+  if (!a || !offsets || !w13 || !w2 || !y_perm || (check_ws && !ws)) return MOE_ERR_NULL;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
   if (rows_cap < 1 || n_ffn < 0 || n_ffn > kMaxFfn || H < 1 || I < 1) return MOE_ERR_SHAPE;
   if (dtype == MOE_BF16 && (H % 128 || I % 64)) return MOE_ERR_SHAPE;
@@ -117,7 +119,7 @@ moe_status ffn_checks(const void* a, const int32_t* offsets, int rows_cap, int n
   if (!aligned(a, al) || !aligned(w13, al) || !aligned(w2, al) || !aligned(y_perm, al) ||
       !aligned(offsets, 4) || !aligned(ws, 256))
     return MOE_ERR_ALIGN;
-  if (ws_bytes < ffn_ws_bytes(rows_cap, n_ffn, I, dtype)) return MOE_ERR_WORKSPACE;
+  if (check_ws && ws_bytes < ffn_ws_bytes(rows_cap, n_ffn, I, dtype)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 }  // namespace
@@ -143,6 +145,25 @@ moe_status moe_expert_ffn_gather(const void* x, int T, int K, const int32_t* row
   if (T < 1 || K < 1 || !fits_i32((long long)T * K)) return MOE_ERR_SHAPE;
   if (!aligned(row_src, 4)) return MOE_ERR_ALIGN;
   if (n_ffn == 0) return MOE_OK;
+  return launched(launch_expert_ffn(x, row_src, K, T, offsets, rows_cap, n_ffn, H, I, w13, w2,
+                                    dtype, y_perm, ws, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_gather_noalloc(const void* x, int T, int K, const int32_t* row_src,
+                                         const int32_t* offsets, int rows_cap, int n_ffn, int H,
+                                         int I, const void* w13, const void* w2, int dtype,
+                                         void* y_perm, void* stream) {
+  if (!row_src) return MOE_ERR_NULL;
+  const moe_status st =
+      ffn_checks(x, offsets, rows_cap, n_ffn, H, I, w13, w2, dtype, y_perm, nullptr, 0, false);
+  if (st != MOE_OK) return st;
+  if (T < 1 || K < 1 || !fits_i32((long long)T * K)) return MOE_ERR_SHAPE;
+  if (!aligned(row_src, 4)) return MOE_ERR_ALIGN;
+  if (ffn_ws_bytes(rows_cap, n_ffn, I, dtype) > MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_TOO_LARGE;
+  if (n_ffn == 0) return MOE_OK;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_LAUNCH;
   return launched(launch_expert_ffn(x, row_src, K, T, offsets, rows_cap, n_ffn, H, I, w13, w2,
                                     dtype, y_perm, ws, (hipStream_t)stream));
 }

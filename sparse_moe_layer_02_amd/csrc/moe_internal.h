@@ -81,6 +81,9 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const in
                           int T, int H, int K, int n_ffn, int32_t* offsets, void* x_perm,
                           int32_t* row_src, int32_t* slot_row, hipStream_t s);
 size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype);
+// Device address, on the current device, of the fixed scratch array of
+// moe_expert_ffn_gather_noalloc (MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES).
+hipError_t noalloc_scratch(void** addr);
 // gather == nullptr: row r's activations are x_perm[r]; otherwise they are
 // token row gather[r] / gK (clamped to [0, gT)) of x_perm, i.e. of x.
 hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, int gT,

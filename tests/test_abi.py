@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
