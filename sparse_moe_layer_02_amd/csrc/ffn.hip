@@ -281,34 +281,76 @@ __device__ __forceinline__ void ffn_consumer(char* smem, int KD, Compute&& compu
   }
 }
 
+// One K step (two 32-wide k blocks) of one compute wave's tile: R row blocks
+// (A rows a_row0 + 16 rb) x C column blocks (weight rows b_row0 + 16 cb) of
+// 16 x 16, v_mfma_f32_16x16x32_bf16 with fp32 accumulators.
+// The fragment reads are software-pipelined: the step runs as groups of two
+// row blocks (2 C MFMAs), and the A fragments of the next group, and at the
+// first group the second k block's B fragments, are read from LDS before the
+// current group's MFMAs issue, so each read has a whole group of MFMAs to
+// land in.  (Read just in time, one wait per two row blocks exposed the LDS
+// latency eight times per K step; the MFMA rate of full tiles was ~40 % of
+// peak.)  Each group starts by waiting for every outstanding LDS read
+// (lgkmcnt(0): only its own fragments are then in flight), so the pipeline
+// holds even where the compiler's own waits are that coarse, as they are in
+// the full tiles' loop of the kernels with wide tiles.  The sched_barriers
+// keep the compiler from sinking the reads to their uses.
+template <int R, int C, class Acc>
+__device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_row0, int b_row0,
+                                         int lane, Acc& acc) {
+  constexpr int kRG = R % 2 == 0 ? 2 : 1;   // row blocks per group
+  constexpr int kNG = 2 * R / kRG;          // groups per step (both k blocks)
+  const int lr = lane & 15, lq = lane >> 4;
+  auto a_frag = [&](int kk, int rb) {
+    const int rA = a_row0 + 16 * rb + lr;
+    return *(const bf16x8*)(As + rA * kRowBytes + swz(rA, kk * 4 + lq) * 16);
+  };
+  auto b_frag = [&](int kk, int cb) {
+    const int rB = b_row0 + 16 * cb + lr;
+    return *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, kk * 4 + lq) * 16);
+  };
+  bf16x8 b[2][C];
+  bf16x8 a[2][kRG];
+#pragma unroll
+  for (int cb = 0; cb < C; ++cb) b[0][cb] = b_frag(0, cb);
+#pragma unroll
+  for (int r = 0; r < kRG; ++r) a[0][r] = a_frag(0, r);
+#pragma unroll
+  for (int g = 0; g < kNG; ++g) {
+    const int kk = (g * kRG) / R, rb0 = (g * kRG) % R;
+    // this group's fragments, read one group ago, have landed; the reads
+    // issued next get the whole group's MFMAs to land in
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < kNG) {
+      const int kn = ((g + 1) * kRG) / R, rn = ((g + 1) * kRG) % R;
+#pragma unroll
+      for (int r = 0; r < kRG; ++r) a[(g + 1) & 1][r] = a_frag(kn, rn + r);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int cb = 0; cb < C; ++cb) b[1][cb] = b_frag(1, cb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kRG; ++r)
+#pragma unroll
+      for (int cb = 0; cb < C; ++cb)
+        acc[rb0 + r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[g & 1][r], b[kk][cb],
+                                                                   acc[rb0 + r][cb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Partial tiles: wave w owns weight rows [16 CB w, +16 CB) (CB 16-column MFMA
-// blocks: 2 of a 128-row tile, 3 of a 192-row one) and all 32G live rows.
+// blocks: 2 of a 128-row tile, 3 of a 192-row one, 4 of a 256-row one) and
+// all 32G live rows.
 template <int G, int CB>
 struct ColumnSplit {
   f32x4 (&acc)[kBmBf16 / 16][CB];
   int wave, lane;
   __device__ __forceinline__ void operator()(const char* As, const char* Bs) const {
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      bf16x8 b[CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int rB = 16 * CB * wave + 16 * cb + (lane & 15);
-        b[cb] = *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, ch) * 16);
-      }
-      bf16x8 a[2 * G];
-#pragma unroll
-      for (int rb = 0; rb < 2 * G; ++rb) {
-        const int rA = rb * 16 + (lane & 15);
-        a[rb] = *(const bf16x8*)(As + rA * kRowBytes + swz(rA, ch) * 16);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 2 * G; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
-    }
+    mma_step<2 * G, CB>(As, Bs, 0, 16 * CB * wave, lane, acc);
   }
 };
 
@@ -320,25 +362,7 @@ struct Quadrant {
   f32x4 (&acc)[8][4];
   int wave, lane;
   __device__ __forceinline__ void operator()(const char* As, const char* Bs) const {
-    const int wr = wave >> 1, wc = wave & 1;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      bf16x8 b[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int rB = 64 * wc + 16 * cb + (lane & 15);
-        b[cb] = *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, ch) * 16);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb) {
-        const int rA = 128 * wr + rb * 16 + (lane & 15);
-        const bf16x8 a = *(const bf16x8*)(As + rA * kRowBytes + swz(rA, ch) * 16);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[cb], acc[rb][cb], 0, 0, 0);
-      }
-    }
+    mma_step<8, 4>(As, Bs, 128 * (wave >> 1), 64 * (wave & 1), lane, acc);
   }
 };
 
@@ -395,9 +419,19 @@ constexpr bool ring_fits(int G, int BN) {
   return kLdsBytes / (32 * G * kRowBytes + BN * kRowBytes) >= 3;
 }
 
+// The K loops a kernel compiles for G live row groups at tile width BN: the
+// wide tiles serve exactly the group counts of the kernel's WIDE_MASK and
+// the 128-row tiles the others.  Only what can run is compiled: with every
+// combination in one kernel, the compiler's wait-count analysis gave up on
+// the full tiles' loop and waited for all outstanding LDS reads before each
+// MFMA group, which undid the fragment-read pipelining there.
+constexpr bool compiled(int G, int BN, int WIDE_MASK) {
+  return ring_fits(G, BN) && (BN == kBN ? !((WIDE_MASK >> G) & 1) : ((WIDE_MASK >> G) & 1));
+}
+
 // One block's work: rows [row0, row0 + rows) of expert e against column
 // tile nt (of NT) of BN weight rows.
-template <bool GATEUP, int BN>
+template <bool GATEUP, int BN, int WIDE_MASK>
 __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A,
                                           const int32_t* __restrict__ gather, int gK, int gT,
                                           const bf16* __restrict__ W, int e, int row0, int rows,
@@ -441,7 +475,7 @@ __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A
     switch (groups) {
 #define MOE_CASE(g) \
       case g:                                                                  \
-        if constexpr (ring_fits(g, BN)) {                                      \
+        if constexpr (compiled(g, BN, WIDE_MASK)) {                            \
           if (GATEUP && src.gather)                                            \
             ffn_loader<g, GATEUP, BN>(smem, src, KD, k_start, wave - 4, lane); \
           else                                                                 \
@@ -500,7 +534,7 @@ __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A
     switch (groups) {
 #define MOE_CASE(g)                                                                 \
       case g:                                                                       \
-        if constexpr (ring_fits(g, BN))                                             \
+        if constexpr (compiled(g, BN, WIDE_MASK))                                   \
           ffn_consumer<g, BN>(smem, KD, ColumnSplit<g, CB>{acc, wave, lane});       \
         break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4)
@@ -539,18 +573,18 @@ __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A
 // One launch per GEMM.  Block -> (m-tile, column slot), XCD-aware: the slots
 // of one m-tile run on one XCD and share its activation rows through that
 // XCD's L2.  Slots count 128-row column tiles; an m-tile whose number of
-// 32-row groups has its bit set in wide_mask takes the wider tiles (BNW
+// 32-row groups has its bit set in WIDE_MASK takes the wider tiles (BNW
 // rows) instead, and its slots past N / BNW exit at once -- cheaper than a
 // second launch for the other tiles (measured: an empty second launch cost
 // 57 us, and two serial launches each drain their own tail; gate/up on the
-// 8192-token layer 5.1-5.2 -> 4.55 ms).  WIDE = false compiles the 128-row
+// 8192-token layer 5.1-5.2 -> 4.55 ms).  WIDE_MASK = 0 compiles the 128-row
 // path alone, for layers with no wide tiles: the kernel with both paths
 // measured 1.5 % slower there (the 16384-token skewed layer's gate/up).
-template <bool GATEUP, bool WIDE>
+template <bool GATEUP, int WIDE_MASK>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
     const bf16* __restrict__ W, const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-    int KD, int I, int H, int NT, int wide_mask, bf16* __restrict__ C) {
+    int KD, int I, int H, int NT, bf16* __restrict__ C) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   constexpr int BNW = GATEUP ? kBNGateUpWide : kBNWide;
   const int b = blockIdx.x;
@@ -561,15 +595,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   const int4 tile = tiles[mt];
   const int e = tile.x, row0 = tile.y, rows = tile.z;
   const int groups = (rows + 31) >> 5;
-  if constexpr (WIDE) {
-    if (((wide_mask >> groups) & 1) && ring_fits(groups, BNW)) {
+  if constexpr (WIDE_MASK != 0) {
+    if ((WIDE_MASK >> groups) & 1) {
       const int ntw = (GATEUP ? 2 * I : H) / BNW;
       if (nt >= ntw) return;
-      ffn_block<GATEUP, BNW>(smem, A, gather, gK, gT, W, e, row0, rows, nt, ntw, KD, I, H, C);
+      ffn_block<GATEUP, BNW, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, nt, ntw, KD,
+                                         I, H, C);
       return;
     }
   }
-  ffn_block<GATEUP, kBN>(smem, A, gather, gK, gT, W, e, row0, rows, nt, NT, KD, I, H, C);
+  ffn_block<GATEUP, kBN, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, nt, NT, KD, I, H,
+                                     C);
 }
 
 // ------------------------------------------------------------ fp32 path --
@@ -708,23 +744,29 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
     // 32 rows even if every pick went to one (decode), every tile is a
     // single group and the kernel without the wide path is launched.
     const bool enough_rows = (long long)rows_cap >= 32LL * n_ffn;
-    const int wide_gu = enough_rows && (2 * I) % kBNGateUpWide == 0 ? kWideGroupsGateUp : 0;
-    const int wide_dn = enough_rows && H % kBNWide == 0 ? kWideGroups : 0;
-#define MOE_GEMMS(W)                                                                     \
-    MOE_LAUNCH("ffn_gateup_bf16", s,                                                       \
-               ffn_mfma_bf16<true, W><<<groups * 8 * nt1, kGemmThreads, 0, s>>>(           \
-                   (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, \
-                   I, H, nt1, wide_gu, (bf16*)hh));                                       \
-    MOE_LAUNCH("ffn_down_bf16", s,                                                         \
-               ffn_mfma_bf16<false, W><<<groups * 8 * nt2, kGemmThreads, 0, s>>>(          \
-                   (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, \
-                   nt2, wide_dn, (bf16*)y_perm))
-    if (wide_gu || wide_dn) {
-      MOE_GEMMS(true);
-    } else {
-      MOE_GEMMS(false);
-    }
-#undef MOE_GEMMS
+    const bool wide_gu = enough_rows && (2 * I) % kBNGateUpWide == 0;
+    const bool wide_dn = enough_rows && H % kBNWide == 0;
+    const unsigned grid_gu = groups * 8 * nt1, grid_dn = groups * 8 * nt2;
+    if (wide_gu)
+      MOE_LAUNCH("ffn_gateup_bf16", s,
+                 ffn_mfma_bf16<true, kWideGroupsGateUp><<<grid_gu, kGemmThreads, 0, s>>>(
+                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
+                     H, nt1, (bf16*)hh));
+    else
+      MOE_LAUNCH("ffn_gateup_bf16", s,
+                 ffn_mfma_bf16<true, 0><<<grid_gu, kGemmThreads, 0, s>>>(
+                     (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
+                     H, nt1, (bf16*)hh));
+    if (wide_dn)
+      MOE_LAUNCH("ffn_down_bf16", s,
+                 ffn_mfma_bf16<false, kWideGroups><<<grid_dn, kGemmThreads, 0, s>>>(
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
+                     (bf16*)y_perm));
+    else
+      MOE_LAUNCH("ffn_down_bf16", s,
+                 ffn_mfma_bf16<false, 0><<<grid_dn, kGemmThreads, 0, s>>>(
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
+                     (bf16*)y_perm));
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
     MOE_LAUNCH("ffn_gateup_f32", s,
