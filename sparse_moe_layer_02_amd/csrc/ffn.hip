@@ -39,6 +39,7 @@
 //     the m-tile's activation rows from that XCD's L2; the column tiles start
 //     their K sweeps at a few different offsets, so that those re-reads are L2
 //     hits rather than 32 simultaneous waits on one miss.
+#include <algorithm>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -63,13 +64,19 @@ constexpr int kBmF32 = 32;
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 // ------------------------------------------------------------ work list --
-// Rows are clamped to [0, rows_cap) and the list to max_tiles entries, so a
+// Rows are clamped to [0, rows_cap) and the lists to their capacities, so a
 // malformed offsets[] can shrink the work but never index past the buffers.
+// Entry: (expert, first row, rows, m-tiles of that expert).  With full != 0,
+// the m-tiles that hold bm rows go to full[] (the dense kernel's list) and
+// only each expert's last, partial m-tile to tiles[].
 __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ offsets, int n_ffn,
                                                   int bm, int rows_cap, int max_tiles,
                                                   int4* __restrict__ tiles,
-                                                  int* __restrict__ ntiles) {
-  __shared__ int part[1024];
+                                                  int* __restrict__ ntiles, int max_full,
+                                                  int4* __restrict__ full,
+                                                  int* __restrict__ nfull) {
+  __shared__ int part[2][1024];
+  __shared__ int full_experts;
   const int tid = threadIdx.x;
   const int per = (n_ffn + 1023) / 1024;
   const int lo = min(n_ffn, tid * per), hi = min(n_ffn, lo + per);
@@ -77,28 +84,50 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
     r0 = min(max(offsets[e], 0), rows_cap);
     m = min(max(offsets[e + 1], r0), rows_cap) - r0;
   };
-  int s = 0;
+  if (tid == 0) full_experts = 0;
+  __syncthreads();
+  int s = 0, f = 0, fe = 0;
   for (int e = lo; e < hi; ++e) {
     int r0, m;
     span(e, r0, m);
-    s += (m + bm - 1) / bm;
+    const int nf = full ? m / bm : 0;
+    f += nf;
+    fe += nf > 0 ? 1 : 0;
+    s += (m + bm - 1) / bm - nf;
   }
-  part[tid] = s;
+  part[0][tid] = s;
+  part[1][tid] = f;
+  if (fe) atomicAdd(&full_experts, fe);
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int v = tid >= off ? part[tid - off] : 0;
+    const int v0 = tid >= off ? part[0][tid - off] : 0;
+    const int v1 = tid >= off ? part[1][tid - off] : 0;
     __syncthreads();
-    part[tid] += v;
+    part[0][tid] += v0;
+    part[1][tid] += v1;
     __syncthreads();
   }
-  int pos = part[tid] - s;
+  int pos = part[0][tid] - s, fpos = part[1][tid] - f;
   for (int e = lo; e < hi; ++e) {
     int r0, m;
     span(e, r0, m);
-    for (int j = 0; j * bm < m && pos < max_tiles; ++j)
-      tiles[pos++] = make_int4(e, r0 + j * bm, min(bm, m - j * bm), 0);
+    const int mt = (m + bm - 1) / bm, nf = full ? m / bm : 0;
+    for (int j = 0; j < mt; ++j) {
+      const int4 t = make_int4(e, r0 + j * bm, min(bm, m - j * bm), mt);
+      if (j < nf) {
+        if (fpos < max_full) full[fpos++] = t;
+      } else if (pos < max_tiles) {
+        tiles[pos++] = t;
+      }
+    }
   }
-  if (tid == 1023) *ntiles = min(part[1023], max_tiles);
+  if (tid == 1023) {
+    *ntiles = min(part[0][1023], max_tiles);
+    if (full) {
+      nfull[0] = min(part[1][1023], max_full);
+      nfull[1] = full_experts;   // experts holding full m-tiles
+    }
+  }
 }
 
 // -------------------------------------------------------- bf16 MFMA GEMM --
@@ -117,7 +146,14 @@ constexpr int kLdsBytes = 160 * 1024;
 // SIMD keeps the matrix core busy.  Writing LDS by DMA (rather than through
 // VGPRs and ds_write) keeps the loader's per-step work to issuing loads.
 typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kCachePolicyNT = 2;   // non-temporal: weights are streamed once
+// Weights are loaded non-temporally when one m-tile holds all of the expert's
+// rows (read once: streamed past the caches) and with the default policy when
+// it has several (its other m-tiles read the same weights again, and the
+// caches keep them: the 256 MB last-level cache holds a heavy expert's 75 MB).
+// Non-temporal weights of a 16,384-row expert made every m-tile fetch them from
+// HBM again (measured: the weight loads alone took 575 us of a 1014 us gate/up
+// GEMM).
+constexpr int kCachePolicyNT = 2;
 
 template <int G, int BN = kBN>
 struct Ring {
@@ -140,6 +176,7 @@ struct TileSrc {
   const bf16* w;        // this expert's weight matrix (row stride KD)
   int nt, I;            // column tile, intermediate size (gate/up pairing)
   bool gateup;
+  bool stream_w;        // the expert has one m-tile: weights non-temporal
   int a_pitch;          // elements between activation rows
   int a_step;           // elements between K steps of one row block
 };
@@ -231,10 +268,14 @@ __device__ __forceinline__ void ffn_loader(char* smem, const TileSrc& t, int KD,
     const bool real = kt < KT;
     const int k0 = real ? k_of(kt) * kBK : 0;
 #pragma unroll
-    for (int i = 0; i < R::kQb; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(real ? src[R::kQa + i] + k0 : t.w),
-                                       (lds_void*)(stage(kt) + R::kABytes + (l + 4 * i) * 1024),
-                                       16, 0, kCachePolicyNT);
+    for (int i = 0; i < R::kQb; ++i) {
+      const void* g = real ? src[R::kQa + i] + k0 : t.w;
+      lds_void* d = (lds_void*)(stage(kt) + R::kABytes + (l + 4 * i) * 1024);
+      if (t.stream_w)
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, kCachePolicyNT);
+      else
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+    }
   };
   auto issue = [&](int kt) {
     issue_a(kt);
@@ -295,9 +336,17 @@ __device__ __forceinline__ void ffn_consumer(char* smem, int KD, Compute&& compu
 // holds even where the compiler's own waits are that coarse, as they are in
 // the full tiles' loop of the kernels with wide tiles.  The sched_barriers
 // keep the compiler from sinking the reads to their uses.
-template <int R, int C, class Acc>
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// hook(g) runs at the start of MFMA group g, after that group's reads are out
+// (the dense kernel issues one of its next step's global->LDS loads there).
+// ONE_B: one set of B fragment registers, reloaded at the first group of the
+// second k block (one exposed LDS latency per step, 4 C fewer registers).
+template <int R, int C, class Acc, class Hook = NoHook, bool ONE_B = false>
 __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_row0, int b_row0,
-                                         int lane, Acc& acc) {
+                                         int lane, Acc& acc, const Hook& hook = Hook{}) {
   constexpr int kRG = R % 2 == 0 ? 2 : 1;   // row blocks per group
   constexpr int kNG = 2 * R / kRG;          // groups per step (both k blocks)
   const int lr = lane & 15, lq = lane >> 4;
@@ -309,7 +358,7 @@ __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_r
     const int rB = b_row0 + 16 * cb + lr;
     return *(const bf16x8*)(Bs + rB * kRowBytes + swz(rB, kk * 4 + lq) * 16);
   };
-  bf16x8 b[2][C];
+  bf16x8 b[ONE_B ? 1 : 2][C];
   bf16x8 a[2][kRG];
 #pragma unroll
   for (int cb = 0; cb < C; ++cb) b[0][cb] = b_frag(0, cb);
@@ -327,17 +376,23 @@ __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_r
 #pragma unroll
       for (int r = 0; r < kRG; ++r) a[(g + 1) & 1][r] = a_frag(kn, rn + r);
     }
-    if (g == 0) {
+    if constexpr (ONE_B) {
+      if (g == kNG / 2) {
+#pragma unroll
+        for (int cb = 0; cb < C; ++cb) b[0][cb] = b_frag(1, cb);
+      }
+    } else if (g == 0) {
 #pragma unroll
       for (int cb = 0; cb < C; ++cb) b[1][cb] = b_frag(1, cb);
     }
+    hook(g);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < kRG; ++r)
 #pragma unroll
       for (int cb = 0; cb < C; ++cb)
-        acc[rb0 + r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[g & 1][r], b[kk][cb],
-                                                                   acc[rb0 + r][cb], 0, 0, 0);
+        acc[rb0 + r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a[g & 1][r], b[ONE_B ? 0 : kk][cb], acc[rb0 + r][cb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -435,7 +490,7 @@ template <bool GATEUP, int BN, int WIDE_MASK>
 __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A,
                                           const int32_t* __restrict__ gather, int gK, int gT,
                                           const bf16* __restrict__ W, int e, int row0, int rows,
-                                          int nt, int NT, int KD, int I, int H,
+                                          bool stream_w, int nt, int NT, int KD, int I, int H,
                                           bf16* __restrict__ C) {
   constexpr int BM = kBmBf16;
   static_assert(BM == 256, "instances cover 8 groups of 32 rows");
@@ -452,7 +507,7 @@ __device__ __forceinline__ void ffn_block(char* smem, const bf16* __restrict__ A
   // columns, one K step of the down GEMM) sit contiguously at
   // row0 * I + j * rows * 64.
   const TileSrc src{gather ? A : A + (size_t)row0 * KD, gather ? gather + row0 : nullptr, gK, gT,
-                    rows, W + (size_t)e * wrows * KD, nt, I, GATEUP,
+                    rows, W + (size_t)e * wrows * KD, nt, I, GATEUP, stream_w,
                     GATEUP ? KD : kBK, GATEUP ? kBK : rows * kBK};
   // The column tiles of one m-tile run side by side on one XCD and read the
   // same activation rows.  Swept in lockstep, every one of them waits on the
@@ -594,18 +649,179 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
   if (mt >= *ntiles) return;
   const int4 tile = tiles[mt];
   const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const bool stream_w = tile.w <= 1;
   const int groups = (rows + 31) >> 5;
   if constexpr (WIDE_MASK != 0) {
     if ((WIDE_MASK >> groups) & 1) {
       const int ntw = (GATEUP ? 2 * I : H) / BNW;
       if (nt >= ntw) return;
-      ffn_block<GATEUP, BNW, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, nt, ntw, KD,
-                                         I, H, C);
+      ffn_block<GATEUP, BNW, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, stream_w, nt,
+                                         ntw, KD, I, H, C);
       return;
     }
   }
-  ffn_block<GATEUP, kBN, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, nt, NT, KD, I, H,
-                                     C);
+  ffn_block<GATEUP, kBN, WIDE_MASK>(smem, A, gather, gK, gT, W, e, row0, rows, stream_w, nt, NT,
+                                     KD, I, H, C);
+}
+
+// ------------------------------------------------- dense full-tile GEMM --
+// Full m-tiles (256 rows of one expert: the experts that hold many tokens,
+// compute-bound) in 256 x 256 blocks, a launch of their own before the other
+// tiles: half the activation bytes per flop of the 256 x 128 quadrant path.
+// On one 16,384-row expert the quadrant path's loads alone took 70 % of its
+// time and its MFMAs alone 50 % (timing-only builds); this kernel takes
+// ~0.80 ms for the gate/up GEMM against ~0.90 ms.
+//   - 8 waves, 2 per SIMD; wave (wr, wc) = (w / 4, w % 4) computes rows
+//     [128 wr, +128) x weight rows [64 wc, +64) (128 accumulator registers);
+//   - no loader waves: each wave issues 8 of a K step's 64 global->LDS loads
+//     (A: 32 groups of 8 rows, B: 32 groups), 2 in each of the first four
+//     MFMA groups of the previous step;
+//   - two stages in two separately declared LDS arrays, loaded and read in
+//     turn: the compiler can tell that the loads into one do not touch the
+//     reads of the other, so no read waits for a load in flight (with one
+//     array it makes every fragment read wait for the wave's newest load);
+//   - measured and not kept: 32-wide K steps with four stages in four arrays
+//     (64-byte rows: 0.93 ms), super-items of 8 m-tiles x 4 weight tiles per
+//     XCD from k = 0 (heavy expert 0.78 ms, but the 64-expert layer's full
+//     tiles 20 % slower);
+//   - gate/up pairing and the m-tile-blocked hh layout as in the other path;
+//     weights cached unless the expert has a single m-tile.
+constexpr int kDenseBN = 256;
+constexpr int kDenseStage = 72 * 1024;   // A 32 KB + B 32 KB of a K step; or half the output
+static_assert(128 * OutTile<kDenseBN>::kPitch <= kDenseStage, "half output tile fits a stage");
+
+// One (full m-tile, 256-row weight tile nt) item of the dense kernel.
+template <bool GATEUP>
+__device__ __forceinline__ void dense_item(char* s0, char* s1, const bf16* __restrict__ A,
+                                           const int32_t* __restrict__ gather, int gK, int gT,
+                                           const bf16* __restrict__ W, int4 tile, int nt,
+                                           int KD, int I, int H, bf16* __restrict__ C) {
+  const int e = tile.x, row0 = tile.y;
+  const bool stream_w = tile.w <= 1;
+  constexpr int BM = kBmBf16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave >> 2, wc = wave & 3;
+  const int KT = KD / kBK;
+  const int k_start = ((nt % 4) * KT) / 4;
+  const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
+  const TileSrc t{gather ? A : A + (size_t)row0 * KD, gather ? gather + row0 : nullptr, gK, gT,
+                  BM, W + (size_t)e * wrows * KD, nt, I, GATEUP, stream_w,
+                  GATEUP ? KD : kBK, GATEUP ? kBK : BM * kBK};
+  // this wave's load groups: A and B groups wave + 8 i, i < 4; lane j of a
+  // group's load fetches chunk swz(row, j & 7) of row 8 g + (j >> 3).  Row
+  // offsets are 32-bit element offsets from the tile's bases (token rows of
+  // x, grouped rows or the m-tile's hh; one expert's weight rows).
+  const int lr = lane >> 3, lc = lane & 7;
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave + 8 * i) * 8 + lr;
+    const int ar = t.gather ? min(max(t.gather[r], 0) / t.gK, t.gT - 1) : r;
+    aoff[i] = (uint32_t)ar * (uint32_t)t.a_pitch + swz(r, lc) * 8;
+    boff[i] = (uint32_t)weight_row<kDenseBN>(t, r) * (uint32_t)KD + swz(r, lc) * 8;
+  }
+  auto k_of = [&](int kt) { const int ks = kt + k_start; return ks >= KT ? ks - KT : ks; };
+  // load u (0..7) of step kt into stage dst: A groups for u < 4, B after
+  auto load = [&](char* dst, int kt, int u) {
+    const int k = k_of(kt);
+    if (u < 4) {
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(t.a_rows + (size_t)k * t.a_step + aoff[u]),
+          (lds_void*)(dst + (wave + 8 * u) * 1024), 16, 0, 0);
+    } else {
+      const void* g = t.w + k * kBK + boff[u - 4];
+      lds_void* d = (lds_void*)(dst + 32768 + (wave + 8 * (u - 4)) * 1024);
+      if (stream_w)
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, kCachePolicyNT);
+      else
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+    }
+  };
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  // one K step from src while step kt_next (if any) loads into dst: two of
+  // this wave's loads in each of the first four MFMA groups, so that their
+  // issue overlaps matrix work and the last of them has half a step to land
+  auto step = [&](const char* src, char* dst, int kt_next) {
+    const bool more = kt_next < KT;
+    auto hook = [&](int g) {
+      if (more && g < 4) {
+        load(dst, kt_next, 2 * g);
+        load(dst, kt_next, 2 * g + 1);
+      }
+    };
+    mma_step<8, 4, decltype(acc), decltype(hook), true>(src, src + 32768, 128 * wr, 64 * wc,
+                                                        lane, acc, hook);
+    wait_vmcnt<0>();   // this wave's loads of the next step have landed
+    lds_barrier();     // ... and everyone's; every wave is done with src
+  };
+#pragma unroll
+  for (int u = 0; u < 8; ++u) load(s0, 0, u);
+  wait_vmcnt<0>();
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(s0, s1, kt + 1);
+    step(s1, s0, kt + 2);
+  }
+  if (kt < KT) step(s0, s1, KT);
+  // Epilogue: each half of the rows goes through its own stage buffer (waves
+  // wr = 0 through s0, wr = 1 through s1) and leaves 16 bytes per lane.
+  constexpr int NC = GATEUP ? kDenseBN / 2 : kDenseBN;
+  const OutTile<NC> out{wr == 0 ? s0 : s1};
+  const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + 4 * q + i;   // row within the half
+      if (GATEUP) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          out.put(r, 32 * wc + 16 * p + c, silu_mul(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]));
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) out.put(r, 64 * wc + 16 * cb + c, acc[rb][cb][i]);
+      }
+    }
+  lds_barrier();
+  const int tid = threadIdx.x & 255;   // the four waves of this half
+  if (GATEUP) {
+    // hh, m-tile-blocked: 64-column block j of the m-tile's 256 rows at
+    // row0 * I + j * 256 * 64; this tile holds blocks 2 nt and 2 nt + 1
+    bf16* dst = C + (size_t)row0 * I;
+    for (int j = tid; j < 128 * OutTile<NC>::kChunks; j += 256) {
+      const int r = j / OutTile<NC>::kChunks, cc = j - r * OutTile<NC>::kChunks;
+      const i32x4 v = *(const i32x4*)(out.t + r * OutTile<NC>::kPitch + cc * 16);
+      bf16* blk = dst + (size_t)(nt * (NC / 64) + (cc >> 3)) * BM * 64;
+      __builtin_nontemporal_store(v, (i32x4*)(blk + (128 * wr + r) * 64 + (cc & 7) * 8));
+    }
+  } else {
+    out.flush(C + (size_t)(row0 + 128 * wr) * H + nt * NC, H, 128, tid);
+  }
+}
+
+// One block per item, XCD-aware (block i on XCD i % 8; the column tiles of
+// one m-tile share that XCD's L2, and their K sweeps start at four offsets
+// so that they do not all wait on one miss).  The grid is sized from the
+// capacity bound of full m-tiles; blocks past the real count exit.
+template <bool GATEUP>
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_dense_bf16(
+    const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
+    const bf16* __restrict__ W, const int4* __restrict__ full, const int* __restrict__ nfull,
+    int KD, int I, int H, int NT, bf16* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char s0[kDenseStage];
+  __shared__ __attribute__((aligned(1024))) char s1[kDenseStage];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NT) * 8 + xcd;
+  const int nt = slot % NT;
+  if (mt >= nfull[0]) return;
+  dense_item<GATEUP>(s0, s1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
 }
 
 // ------------------------------------------------------------ fp32 path --
@@ -678,6 +894,12 @@ __global__ __launch_bounds__(kThreads) void ffn_f32(const float* __restrict__ A,
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline int ffn_bm(int dtype) { return dtype == MOE_BF16 ? kBmBf16 : kBmF32; }
 inline size_t max_mtiles(int rows_cap, int n_ffn, int bm) { return (size_t)rows_cap / bm + n_ffn + 8; }
+inline size_t max_full(int rows_cap) { return (size_t)rows_cap / kBmBf16 + 1; }
+// Full m-tiles go to the dense kernel when both GEMMs' weight rows split
+// into its 256-row tiles (bf16 only).
+inline bool dense_shapes(int dtype, int H, int I) {
+  return dtype == MOE_BF16 && (2 * I) % kDenseBN == 0 && H % kDenseBN == 0;
+}
 
 }  // namespace
 
@@ -709,9 +931,12 @@ hipError_t noalloc_scratch(void** addr) {
   return hipSuccess;
 }
 
+// Workspace: [0, 256) the two tile counts; the tile list; the full-tile
+// list (bf16); hh [rows_cap][I].
 size_t ffn_ws_bytes(int rows_cap, int n_ffn, int I, int dtype) {
   const int es = dtype == MOE_BF16 ? 2 : 4;
   return 256 + align256(max_mtiles(rows_cap, n_ffn, ffn_bm(dtype)) * sizeof(int4)) +
+         (dtype == MOE_BF16 ? align256(max_full(rows_cap) * sizeof(int4)) : 0) +
          align256((size_t)rows_cap * I * es);
 }
 
@@ -721,15 +946,38 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
                              hipStream_t s) {
   const int bm = ffn_bm(dtype);
   const size_t mtmax = max_mtiles(rows_cap, n_ffn, bm);
+  const size_t fmax = dtype == MOE_BF16 ? max_full(rows_cap) : 0;
   int* ntiles = (int*)ws;
+  int* nfull = (int*)ws + 1;
   int4* tiles = (int4*)((char*)ws + 256);
-  void* hh = (char*)ws + 256 + align256(mtmax * sizeof(int4));
+  int4* full = (int4*)((char*)tiles + align256(mtmax * sizeof(int4)));
+  void* hh = (char*)full + align256(fmax * sizeof(int4));
+  // An expert holds at most one row per token: the gather path knows the
+  // tokens, so a batch of fewer than 256 tokens has no full m-tile.
+  const int rows_per_expert = gather ? min(rows_cap, gT) : rows_cap;
+  // (and the dense kernel's 32-bit row offsets must fit: token rows of x and
+  // weight rows of one expert)
+  const bool dense = dense_shapes(dtype, H, I) && rows_per_expert >= kBmBf16 &&
+                     (size_t)(gather ? gT : kBmBf16) * H < ((size_t)1 << 31) &&
+                     (size_t)2 * I * H < ((size_t)1 << 31);
   MOE_LAUNCH("ffn_tiles", s,
              ffn_tiles<<<1, 1024, 0, s>>>(offsets, n_ffn, bm, rows_cap, (int)mtmax, tiles,
-                                          ntiles));
+                                          ntiles, (int)fmax, dense ? full : nullptr, nfull));
   if (dtype == MOE_BF16) {
-    const unsigned groups = ceil_div(mtmax, 8);
+    // with the full m-tiles in the dense kernel, at most one m-tile per
+    // expert is left for this one
+    const unsigned groups = ceil_div(dense ? std::min(mtmax, (size_t)n_ffn) : mtmax, 8);
     const int nt1 = I / 64, nt2 = H / kBN;
+    const unsigned dense_groups = ceil_div(fmax, 8) * 8;   // full m-tiles, rounded to 8 XCDs
+    if (dense) {
+      const unsigned dense_grid = dense_groups * (2 * I / kDenseBN);
+      // the full m-tiles: 256 x 256 blocks, before the other tiles
+      MOE_LAUNCH("ffn_gateup_dense_bf16", s,
+                 ffn_dense_bf16<true><<<dense_grid, kGemmThreads, 0, s>>>(
+                                                (const bf16*)x_perm, gather, gK, gT,
+                                                (const bf16*)w13, full, nfull, H, I, H,
+                                                2 * I / kDenseBN, (bf16*)hh));
+    }
     // Partial m-tiles take wider weight tiles, which cut the activation
     // traffic from L2 per weight byte:
     //   gate/up: 256 rows (128 hh columns) for tiles of 2-5 groups, whose
@@ -757,6 +1005,12 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
                  ffn_mfma_bf16<true, 0><<<grid_gu, kGemmThreads, 0, s>>>(
                      (const bf16*)x_perm, gather, gK, gT, (const bf16*)w13, tiles, ntiles, H, I,
                      H, nt1, (bf16*)hh));
+    if (dense)
+      MOE_LAUNCH("ffn_down_dense_bf16", s,
+                 ffn_dense_bf16<false><<<dense_groups * (H / kDenseBN), kGemmThreads, 0, s>>>(
+                                              (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2,
+                                              full, nfull, I, I, H, H / kDenseBN,
+                                              (bf16*)y_perm));
     if (wide_dn)
       MOE_LAUNCH("ffn_down_bf16", s,
                  ffn_mfma_bf16<false, kWideGroups><<<grid_dn, kGemmThreads, 0, s>>>(
