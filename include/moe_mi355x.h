@@ -276,7 +276,12 @@ moe_status moe_router_similarity(const float *w_router, int E, int H, float *sim
  * kernels named in a comma-separated list (NULL or "": every kernel) and
  * returns the number of names; each bracketed launch costs a few
  * microseconds of stream time, so timed loops select what they need.  The
- * session is process-wide; concurrent callers share it. */
+ * session is process-wide; concurrent callers share it.
+ * Graph capture: while the timing is off (the default) a launch reads one
+ * atomic flag and records nothing, so every call above can be captured into
+ * a HIP graph.  Do not enable it around a capture: the events recorded then
+ * become graph nodes, the session's records refer to events that only the
+ * graph's replays complete, and moe_profile_summary may report -1. */
 int moe_profile_enable(int on);
 int moe_profile_select(const char *names);
 int moe_profile_summary(char *buf, size_t len);
