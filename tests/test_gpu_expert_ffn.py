@@ -16,7 +16,7 @@ from _parity import THREADS, TOL, device, host, normwise
 
 pytestmark = pytest.mark.gpu
 
-ROWS = [1, 40, 70, 100, 150, 200, 224, 230, 256, 300, 513, 17]
+ROWS = [1, 40, 70, 100, 150, 180, 200, 224, 230, 256, 300, 513, 17]
 
 
 @pytest.mark.parametrize("H,I", [(384, 128), (768, 256), (640, 192), (1024, 256)])
