@@ -107,6 +107,11 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
     part[1][tid] += v1;
     __syncthreads();
   }
+  // With full m-tiles split off, tiles[] lists the experts in reverse order:
+  // the dense kernel has just read the experts' weights in expert order, so
+  // the last ones are the likeliest to still sit in the last-level cache
+  // when the other m-tiles read them again.
+  const int ntot = min(part[0][1023], max_tiles);
   int pos = part[0][tid] - s, fpos = part[1][tid] - f;
   for (int e = lo; e < hi; ++e) {
     int r0, m;
@@ -116,13 +121,14 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
       const int4 t = make_int4(e, r0 + j * bm, min(bm, m - j * bm), mt);
       if (j < nf) {
         if (fpos < max_full) full[fpos++] = t;
-      } else if (pos < max_tiles) {
-        tiles[pos++] = t;
+      } else if (pos < ntot) {
+        tiles[full ? ntot - 1 - pos : pos] = t;
+        ++pos;
       }
     }
   }
   if (tid == 1023) {
-    *ntiles = min(part[0][1023], max_tiles);
+    *ntiles = ntot;
     if (full) {
       nfull[0] = min(part[1][1023], max_full);
       nfull[1] = full_experts;   // experts holding full m-tiles
