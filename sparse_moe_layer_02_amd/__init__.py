@@ -110,6 +110,14 @@ def _want(t, dtype, name):
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
+def _require(ok, what):
+    # shape checks the C calls cannot make themselves (they see pointers and
+    # the sizes passed in); a failed one would let a kernel read or write
+    # past a buffer, so it raises whatever the interpreter's flags
+    if not ok:
+        raise ValueError(f"argument check failed: {what}")
+
+
 # --------------------------------------------------------------- the calls --
 
 def moe_router_logits(x, w_router, logits, w_planes=None):
@@ -121,13 +129,14 @@ def moe_router_logits(x, w_router, logits, w_planes=None):
     _want(logits, torch.float32, "logits")
     T, H = x.shape
     E = w_router.shape[0]
-    assert w_router.shape == (E, H) and logits.shape == (T, E)
+    _require(w_router.shape == (E, H) and logits.shape == (T, E),
+             "w_router.shape == (E, H) and logits.shape == (T, E)")
     if w_planes is None:
         _check("moe_router_logits", lib().moe_router_logits(
             _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
         return
     _want(w_planes, torch.bfloat16, "w_planes")
-    assert w_planes.shape == (3, E, H)
+    _require(w_planes.shape == (3, E, H), "w_planes.shape == (3, E, H)")
     _check("moe_router_logits_planes", lib().moe_router_logits_planes(
         _ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(w_planes), T, H, E, _ptr(logits),
         _stream(x)))
@@ -141,7 +150,7 @@ def moe_router_split_weights(w_router, w_planes):
     _want(w_router, torch.float32, "w_router")
     _want(w_planes, torch.bfloat16, "w_planes")
     E, H = w_router.shape
-    assert w_planes.shape == (3, E, H)
+    _require(w_planes.shape == (3, E, H), "w_planes.shape == (3, E, H)")
     _check("moe_router_split_weights", lib().moe_router_split_weights(
         _ptr(w_router), E, H, _ptr(w_planes), _stream(w_router)))
 
@@ -167,8 +176,9 @@ def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
     _want(topk_idx, torch.int32, "topk_idx")
     _want(topk_gate, torch.float32, "topk_gate")
     _want(counts, torch.int32, "counts")
-    assert bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K)
-    assert counts.shape == (E,)
+    _require(bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K),
+             "bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K)")
+    _require(counts.shape == (E,), "counts.shape == (E,)")
     _check("moe_route", lib().moe_route(
         _ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
         _ptr(dev_status), _stream(logits)))
@@ -185,10 +195,13 @@ def moe_permute(x, topk_idx, counts, n_ffn, offsets, x_perm, row_src, slot_row):
         _want(t, torch.int32, n)
     T, H = x.shape
     K = topk_idx.shape[1]
-    assert topk_idx.shape[0] == T and row_src.numel() >= T * K and slot_row.numel() >= T * K
-    assert counts.numel() >= n_ffn and offsets.numel() >= n_ffn + 1
+    _require(topk_idx.shape[0] == T and row_src.numel() >= T * K and slot_row.numel() >= T * K,
+             "topk_idx.shape[0] == T and row_src.numel() >= T * K and slot_row.numel() >= T * K")
+    _require(counts.numel() >= n_ffn and offsets.numel() >= n_ffn + 1,
+             "counts.numel() >= n_ffn and offsets.numel() >= n_ffn + 1")
     if x_perm is not None:
-        assert x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K
+        _require(x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K,
+                 "x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K")
     _check("moe_permute", lib().moe_permute(
         _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), _ptr(counts),
         T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row),
@@ -205,8 +218,10 @@ def moe_expert_ffn(x_perm, offsets, w13, w2, y_perm, ws):
     rows_cap, H = x_perm.shape
     N, I2, H2 = w13.shape
     I = I2 // 2
-    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape == x_perm.shape
-    assert w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype
+    _require(H2 == H and w2.shape == (N, H, I) and y_perm.shape == x_perm.shape,
+             "H2 == H and w2.shape == (N, H, I) and y_perm.shape == x_perm.shape")
+    _require(w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype,
+             "w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype")
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(x_perm), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2), _DT[x_perm.dtype],
         _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x_perm)))
@@ -220,9 +235,11 @@ def moe_expert_ffn_gather(x, K, row_src, offsets, w13, w2, y_perm, ws):
     rows_cap = y_perm.shape[0]
     N, I2, H2 = w13.shape
     I = I2 // 2
-    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H
-    assert row_src.numel() >= rows_cap
-    assert w13.dtype == w2.dtype == x.dtype == y_perm.dtype
+    _require(H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H,
+             "H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H")
+    _require(row_src.numel() >= rows_cap, "row_src.numel() >= rows_cap")
+    _require(w13.dtype == w2.dtype == x.dtype == y_perm.dtype,
+             "w13.dtype == w2.dtype == x.dtype == y_perm.dtype")
     _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
         _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
         _DT[x.dtype], _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
@@ -241,9 +258,11 @@ def moe_expert_ffn_gather_noalloc(x, K, row_src, offsets, w13, w2, y_perm):
     rows_cap = y_perm.shape[0]
     N, I2, H2 = w13.shape
     I = I2 // 2
-    assert H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H
-    assert row_src.numel() >= rows_cap
-    assert w13.dtype == w2.dtype == x.dtype == y_perm.dtype
+    _require(H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H,
+             "H2 == H and w2.shape == (N, H, I) and y_perm.shape[1] == H")
+    _require(row_src.numel() >= rows_cap, "row_src.numel() >= rows_cap")
+    _require(w13.dtype == w2.dtype == x.dtype == y_perm.dtype,
+             "w13.dtype == w2.dtype == x.dtype == y_perm.dtype")
     _check("moe_expert_ffn_gather_noalloc", lib().moe_expert_ffn_gather_noalloc(
         _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
         _DT[x.dtype], _ptr(y_perm), _stream(x)))
@@ -257,7 +276,8 @@ def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
     _want(topk_idx, torch.int32, "topk_idx")
     _want(topk_gate, torch.float32, "topk_gate")
     _want(y_acc, torch.float32, "y_acc")
-    assert topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H)
+    _require(topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H),
+             "topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H)")
     _check("moe_zero_experts", lib().moe_zero_experts(
         _ptr(x), _DT[x.dtype], _ptr(topk_idx), _ptr(topk_gate), T, H, K, n_ffn, _ptr(y_acc),
         _stream(x)))
@@ -270,8 +290,10 @@ def _combine_args(y_perm, slot_row, topk_gate, y):
     K = topk_gate.shape[1]
     _want(slot_row, torch.int32, "slot_row")
     _want(topk_gate, torch.float32, "topk_gate")
-    assert topk_gate.shape == (T, K) and slot_row.numel() >= T * K
-    assert y_perm.dim() == 2 and y_perm.shape[1] == H and y_perm.dtype == y.dtype
+    _require(topk_gate.shape == (T, K) and slot_row.numel() >= T * K,
+             "topk_gate.shape == (T, K) and slot_row.numel() >= T * K")
+    _require(y_perm.dim() == 2 and y_perm.shape[1] == H and y_perm.dtype == y.dtype,
+             "y_perm.dim() == 2 and y_perm.shape[1] == H and y_perm.dtype == y.dtype")
     return T, H, K
 
 
@@ -280,7 +302,7 @@ def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
     _dev(y_perm, slot_row, topk_gate, y_acc, y)
     T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
     _want(y_acc, torch.float32, "y_acc")
-    assert y_acc.shape == (T, H)
+    _require(y_acc.shape == (T, H), "y_acc.shape == (T, H)")
     _check("moe_combine", lib().moe_combine(
         _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
@@ -291,7 +313,7 @@ def moe_combine_identity(y_perm, x, slot_row, topk_gate, ffn_scale, y):
     slots' gates) * x + sum of ffn_scale * gate * y_perm rows, in slot order."""
     _dev(y_perm, x, slot_row, topk_gate, y)
     T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
-    assert x.shape == (T, H) and x.dtype == y.dtype
+    _require(x.shape == (T, H) and x.dtype == y.dtype, "x.shape == (T, H) and x.dtype == y.dtype")
     _check("moe_combine_identity", lib().moe_combine_identity(
         _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
         T, H, K, _ptr(y), _stream(y)))
@@ -303,8 +325,10 @@ def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_e
     _want(counts, torch.int32, "counts")
     for t, n in ((bias, "bias"), (integral, "integral"), (prev_err, "prev_err")):
         _want(t, torch.float32, n)
-    assert counts.numel() >= n_ffn and bias.numel() >= n_ffn
-    assert integral.numel() >= n_ffn and prev_err.numel() >= n_ffn
+    _require(counts.numel() >= n_ffn and bias.numel() >= n_ffn,
+             "counts.numel() >= n_ffn and bias.numel() >= n_ffn")
+    _require(integral.numel() >= n_ffn and prev_err.numel() >= n_ffn,
+             "integral.numel() >= n_ffn and prev_err.numel() >= n_ffn")
     _check("moe_bias_update", lib().moe_bias_update(
         _ptr(counts), int(T), int(n_ffn), float(target), float(kp), float(ki), float(kd),
         _ptr(bias), _ptr(integral), _ptr(prev_err), _stream(bias)))
@@ -322,8 +346,9 @@ def moe_router_similarity(w_router, sim, mean, ws):
     _want(sim, torch.float32, "sim")
     _want(mean, torch.float32, "mean")
     E, H = w_router.shape
-    assert sim.shape == (E, E) and mean.numel() >= 1
-    assert w_router.is_contiguous() and sim.is_contiguous()
+    _require(sim.shape == (E, E) and mean.numel() >= 1, "sim.shape == (E, E) and mean.numel() >= 1")
+    _require(w_router.is_contiguous() and sim.is_contiguous(),
+             "w_router.is_contiguous() and sim.is_contiguous()")
     _check("moe_router_similarity", lib().moe_router_similarity(
         _ptr(w_router), E, H, _ptr(sim), _ptr(mean), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(w_router)))
