@@ -163,18 +163,34 @@ def routing_stats(cfg, counts, S):
                                         "max": int(act.max()) if act.size else 0})
 
 
+def code_sha256(path):
+    """SHA-256 of a C++/HIP source with its // comments, trailing blanks and
+    empty lines removed: the same for two versions that differ only in their
+    comments (which compile to the same kernels)."""
+    out = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            i = line.find("//")
+            if i >= 0:
+                line = line[:i]
+            line = line.rstrip()
+            if line:
+                out.append(line)
+    return hashlib.sha256("\n".join(out).encode()).hexdigest()
+
+
 def measured_traffic(workload_name):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE, scaled by a plain-copy calibration), or None
-    if they were taken on another workload or another version of the kernel."""
+    if they were taken on another workload or another version of the kernel
+    (compared by code_sha256 of the GEMM source)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(FFN_SOURCE, "rb") as f:
-            src = hashlib.sha256(f.read()).hexdigest()
+        src = code_sha256(FFN_SOURCE)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != src or rec.get("workload") != workload_name:
+    if rec.get("code_sha256") != src or rec.get("workload") != workload_name:
         return None
     return int(rec["bytes_per_launch"])
 

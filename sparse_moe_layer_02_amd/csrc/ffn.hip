@@ -38,7 +38,11 @@
 //     in turn, so all column tiles of one m-tile run on one XCD and re-read
 //     the m-tile's activation rows from that XCD's L2; the column tiles start
 //     their K sweeps at a few different offsets, so that those re-reads are L2
-//     hits rather than 32 simultaneous waits on one miss.
+//     hits rather than 32 simultaneous waits on one miss;
+//   - the full 256-row m-tiles of experts that hold at least 256 rows (the
+//     compute-bound regime) go to a kernel of their own, launched before the
+//     other tiles of each GEMM: 256 x 256 blocks whose eight waves all compute
+//     (the dense kernel, below).
 #include <algorithm>
 #include <mutex>
 
