@@ -1,7 +1,8 @@
 """The allocation-free expert-FFN entry point (moe_expert_ffn_gather_noalloc)
 against moe_expert_ffn_gather, through the C ABI: bit for bit on two calls in
 a row, the second with a smaller batch (the fixed scratch keeps the first
-call's contents), and a too-large batch rejected before any launch."""
+call's contents), a too-large batch rejected before any launch, and the call
+captured into a HIP graph and replayed."""
 import numpy as np
 import pytest
 import torch
@@ -62,3 +63,39 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
     st = f(p, 16, 1, p, p, rows, N, H, I, p, p, 1, p, None)
     assert st == 7, st                             # MOE_ERR_TOO_LARGE
     assert moe.lib().moe_status_string(7) == b"sizes exceed the fixed scratch"
+
+
+def test_noalloc_call_captured_in_a_graph():
+    """The entry point's purpose: captured into a HIP graph (its scratch
+    address is looked up by the eager call before the capture) and replayed,
+    it gives the eager result bit for bit on every replay."""
+    dev = device()
+    inp = workload.make_inputs(CFG, dev)
+    buf = _routed(CFG, inp, dev)
+    rows = CFG.T * CFG.K
+    y = torch.empty((rows, CFG.H), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        moe.moe_expert_ffn_gather_noalloc(inp["x"], CFG.K, buf["row_src"], buf["offsets"],
+                                          inp["w13"], inp["w2"], y)
+
+    call()
+    torch.cuda.synchronize()
+    S = int(host(buf["offsets"])[-1])
+    ref = y[:S].clone()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y[:S], ref), rep
