@@ -143,6 +143,8 @@ moe_status moe_permute(const void *x, int dtype, const int32_t *topk_idx, const 
  * written.  fp32 accumulation; for MOE_BF16, hh is rounded to bf16 between
  * the two GEMMs and y_perm is stored in bf16.
  * MOE_BF16 requires H % 128 == 0 and I % 64 == 0.
+ * n_ffn == 0 (a pool of zero-computation experts only) enqueues nothing;
+ * w13 and w2 may then be NULL.
  * ws: at least moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype). */
 size_t moe_expert_ffn_workspace_bytes(int rows_cap, int n_ffn, int I, int dtype);
 moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, int rows_cap,

@@ -110,7 +110,8 @@ namespace {
 moe_status ffn_checks(const void* a, const int32_t* offsets, int rows_cap, int n_ffn, int H, int I,
                       const void* w13, const void* w2, int dtype, const void* y_perm,
                       const void* ws, size_t ws_bytes, bool check_ws = true) {
-  if (!a || !offsets || !w13 || !w2 || !y_perm || (check_ws && !ws)) return MOE_ERR_NULL;
+  if (!a || !offsets || (n_ffn != 0 && (!w13 || !w2)) || !y_perm || (check_ws && !ws))
+    return MOE_ERR_NULL;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
   if (rows_cap < 1 || n_ffn < 0 || n_ffn > kMaxFfn || H < 1 || I < 1) return MOE_ERR_SHAPE;
   if (dtype == MOE_BF16 && (H % 128 || I % 64)) return MOE_ERR_SHAPE;

@@ -131,6 +131,8 @@ def test_expert_ffn_validation():
     assert f(*a) == DTYPE
     a = list(args); a[3] = 0                      # no FFN experts: nothing to do
     assert f(*a) == OK
+    a[6] = a[7] = None                            # ... and no weights needed
+    assert f(*a) == OK
 
 
 def test_expert_ffn_gather_validation():
@@ -156,6 +158,8 @@ def test_expert_ffn_gather_validation():
     a = list(args); a[14] = need - 1
     assert f(*a) == WS
     a = list(args); a[6] = 0                      # no FFN experts: nothing to do
+    assert f(*a) == OK
+    a[9] = a[10] = None                           # ... and no weights needed
     assert f(*a) == OK
 
 

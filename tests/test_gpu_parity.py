@@ -43,6 +43,24 @@ def _e2e(cfg, inp, buf, tokens=None):
     return err
 
 
+@pytest.mark.parametrize("N,Z,base", [(16, 0, "tiny_fp32"), (0, 16, "tiny_fp32"),
+                                      (24, 0, "mid_bf16"), (0, 24, "mid_bf16")])
+@pytest.mark.parametrize("path", list(PATHS))
+def test_pool_of_one_expert_kind(N, Z, base, path):
+    """Degenerate pools: FFN experts only (an ordinary MoE layer, Z = 0) and
+    zero-computation experts only (N = 0: no FFN rows, the expert GEMMs
+    enqueue nothing and y = x times the summed gates)."""
+    cfg = workload.CONFIGS[base].replace(N=N, Z=Z, T=200)
+    inp, buf = _run(cfg, path=path)
+    S = int(host(buf["offsets"])[-1])
+    assert S == (200 * cfg.K if Z == 0 else 0)
+    if N == 0:
+        g = host(buf["topk_gate"]).astype(np.float64).sum(1)
+        ref = inputs_on_host(inp)["x"].astype(np.float64) * g[:, None]
+        assert normwise(host(buf["y"]), ref) <= TOL[cfg.dtype]
+    _e2e(cfg, inp, buf)
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 def test_tiny_fp32_layer(path):
     cfg = workload.CONFIGS["tiny_fp32"]
