@@ -45,7 +45,8 @@ CALLS = {
     "moe_route": ("route_topk", "route_hist"),
     "moe_permute": ("permute", "permute_gather"),
     "moe_expert_ffn": ("ffn_tiles", "ffn_gateup_dense_bf16", "ffn_gateup_bf16",
-                       "ffn_down_dense_bf16", "ffn_down_bf16", "ffn_gateup_f32", "ffn_down_f32"),
+                       "ffn_down_dense_bf16", "ffn_down_narrow_bf16", "ffn_down_bf16",
+                       "ffn_gateup_f32", "ffn_down_f32"),
     "moe_zero_experts": ("zero_experts",),
     "moe_combine": ("combine",),
     "moe_combine_identity": ("combine_identity",),
@@ -340,10 +341,11 @@ def time_workload(cfg, inp, args, dev, x=None, bias=None, steps=None, warmup=Non
     # ~80 us of stream time per step (measured).  The per-call table comes
     # from a separate pass afterwards.
     # each expert GEMM is one launch for the partial m-tiles plus, on bf16
-    # layers, one for the full 256-row m-tiles (the dense kernel)
+    # layers, one for the full 256-row m-tiles (the dense kernel), and for
+    # down one more for the partial m-tiles of at most 128 rows
     gemm_names = ((("ffn_gateup_bf16", "ffn_gateup_dense_bf16"),
-                   ("ffn_down_bf16", "ffn_down_dense_bf16")) if cfg.dtype == "bf16"
-                  else (("ffn_gateup_f32",), ("ffn_down_f32",)))
+                   ("ffn_down_bf16", "ffn_down_dense_bf16", "ffn_down_narrow_bf16"))
+                  if cfg.dtype == "bf16" else (("ffn_gateup_f32",), ("ffn_down_f32",)))
     moe.moe_profile_select(gemm_names[0] + gemm_names[1])
     moe.moe_profile_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -462,7 +464,7 @@ def main():
     achieved = alg["gateup_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(cfg.name),
-                    kernel=" + ".join(r["gemm_names"][0]), kernel_ms=round(r["gu_ms"], 4),
+                    kernel=" + ".join(n for n in r["gemm_names"][0] if n in r["kern_timed"]), kernel_ms=round(r["gu_ms"], 4),
                     algorithmic_bytes=alg["gateup_bytes"], mfma_frac=gu["mfma_frac"])
     prof_ms = r["prof_ms"]
     result = {

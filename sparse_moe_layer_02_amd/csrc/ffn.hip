@@ -72,14 +72,17 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // malformed offsets[] can shrink the work but never index past the buffers.
 // Entry: (expert, first row, rows, m-tiles of that expert).  With full != 0,
 // the m-tiles that hold bm rows go to full[] (the dense kernel's list) and
-// only each expert's last, partial m-tile to tiles[].
+// only each expert's last, partial m-tile to tiles[].  tiles[] holds first
+// the m-tiles of more than narrow_rows rows, then those of at most
+// narrow_rows (narrow_rows = 0: all in the first part); counts: ntiles[0] =
+// all of them, ntiles[3] = the first part, ntiles[4] = the second.
 __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ offsets, int n_ffn,
                                                   int bm, int rows_cap, int max_tiles,
                                                   int4* __restrict__ tiles,
                                                   int* __restrict__ ntiles, int max_full,
                                                   int4* __restrict__ full,
-                                                  int* __restrict__ nfull) {
-  __shared__ int part[2][1024];
+                                                  int* __restrict__ nfull, int narrow_rows) {
+  __shared__ int part[3][1024];
   __shared__ int full_experts;
   const int tid = threadIdx.x;
   const int per = (n_ffn + 1023) / 1024;
@@ -90,49 +93,62 @@ __global__ __launch_bounds__(1024) void ffn_tiles(const int32_t* __restrict__ of
   };
   if (tid == 0) full_experts = 0;
   __syncthreads();
-  int s = 0, f = 0, fe = 0;
+  // only an expert's last m-tile can be short: it is narrow when it holds
+  // at most narrow_rows rows
+  auto n_narrow = [&](int m) { return m > 0 && m % bm != 0 && m % bm <= narrow_rows ? 1 : 0; };
+  int s = 0, f = 0, n = 0, fe = 0;
   for (int e = lo; e < hi; ++e) {
     int r0, m;
     span(e, r0, m);
-    const int nf = full ? m / bm : 0;
+    const int nf = full ? m / bm : 0, nn = n_narrow(m);
     f += nf;
+    n += nn;
     fe += nf > 0 ? 1 : 0;
-    s += (m + bm - 1) / bm - nf;
+    s += (m + bm - 1) / bm - nf - nn;
   }
   part[0][tid] = s;
   part[1][tid] = f;
+  part[2][tid] = n;
   if (fe) atomicAdd(&full_experts, fe);
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int v0 = tid >= off ? part[0][tid - off] : 0;
     const int v1 = tid >= off ? part[1][tid - off] : 0;
+    const int v2 = tid >= off ? part[2][tid - off] : 0;
     __syncthreads();
     part[0][tid] += v0;
     part[1][tid] += v1;
+    part[2][tid] += v2;
     __syncthreads();
   }
-  // With full m-tiles split off, tiles[] lists the experts in reverse order:
-  // the dense kernel has just read the experts' weights in expert order, so
-  // the last ones are the likeliest to still sit in the last-level cache
-  // when the other m-tiles read them again.
-  const int ntot = min(part[0][1023], max_tiles);
-  int pos = part[0][tid] - s, fpos = part[1][tid] - f;
+  // With full m-tiles split off, each part of tiles[] lists the experts in
+  // reverse order: the dense kernel has just read the experts' weights in
+  // expert order, so the last ones are the likeliest to still sit in the
+  // last-level cache when the other m-tiles read them again.
+  const int nw = min(part[0][1023], max_tiles);
+  const int nn = min(part[2][1023], max_tiles - nw);
+  int pos = part[0][tid] - s, fpos = part[1][tid] - f, npos = part[2][tid] - n;
   for (int e = lo; e < hi; ++e) {
     int r0, m;
     span(e, r0, m);
-    const int mt = (m + bm - 1) / bm, nf = full ? m / bm : 0;
+    const int mt = (m + bm - 1) / bm, nf = full ? m / bm : 0, nar = n_narrow(m);
     for (int j = 0; j < mt; ++j) {
       const int4 t = make_int4(e, r0 + j * bm, min(bm, m - j * bm), mt);
       if (j < nf) {
         if (fpos < max_full) full[fpos++] = t;
-      } else if (pos < ntot) {
-        tiles[full ? ntot - 1 - pos : pos] = t;
+      } else if (nar && j == mt - 1) {
+        if (npos < nn) tiles[nw + (full ? nn - 1 - npos : npos)] = t;
+        ++npos;
+      } else {
+        if (pos < nw) tiles[full ? nw - 1 - pos : pos] = t;
         ++pos;
       }
     }
   }
   if (tid == 1023) {
-    *ntiles = ntot;
+    ntiles[0] = nw + nn;
+    ntiles[3] = nw;
+    ntiles[4] = nn;
     if (full) {
       nfull[0] = min(part[1][1023], max_full);
       nfull[1] = full_experts;   // experts holding full m-tiles
@@ -834,6 +850,150 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_dense_bf16(
   dense_item<GATEUP>(s0, s1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
 }
 
+// ----------------------- down GEMM: 512-row weight tiles, at most 128 rows --
+// The down GEMM's last m-tiles of at most 4 row groups (at most 128 rows:
+// half of the full-scale prefill layer's experts) against 512-row weight
+// tiles, in a launch of their own between the dense kernel and the main
+// one.  Every column tile re-reads the m-tile's hh rows from L2, and those
+// loads hold the same per-CU request slots as the weight stream: at 192
+// weight rows per tile every weight byte brings two thirds of a byte of
+// them, at 512 a quarter.  Accumulators for 128 rows x 512 weight rows need
+// eight compute waves, 64 weight rows each; the loads stay on four waves of
+// their own (12 waves, 3 per SIMD, 168 registers each), so that a stalled
+// 1 KB DMA issue never holds a matrix core.  Two 80 KB stages in two
+// separately declared arrays, one step in flight, one barrier per step.
+// Measured on 64 experts of 128 rows at the prefill shape: 297-304 us
+// against 340-350 us for the main kernel's 192-row tiles.  (The same kernel
+// for gate/up, K = 6144, was 7-11 % slower than the main kernel's 256-row
+// tiles and is not used there.)
+constexpr int kW12Threads = 768;
+constexpr int kW12BN = 512;
+constexpr int kW12Stage = 80 * 1024;
+constexpr int kW12MaxRows = 128;
+// Buffer descriptor word 3 for raw 32-bit buffer loads on gfx9 parts (data
+// format 32, no swizzle, no index stride).
+constexpr int kBufferFlags = 0x00020000;
+static_assert(64 * OutTile<kW12BN>::kPitch <= kW12Stage, "half the output tile fits a stage");
+
+template <int G>
+__device__ __forceinline__ void down512_item(char* s0, char* s1, const bf16* __restrict__ hh,
+                                             const bf16* __restrict__ W, int4 tile, int nt,
+                                             int I, int H, bf16* __restrict__ C) {
+  constexpr int BN = kW12BN, R = 2 * G;
+  constexpr int NA = 4 * G;                  // 8-row hh groups of a step
+  constexpr int QB = BN / 8 / 4;             // weight groups per loader per step (16)
+  using Out = OutTile<BN>;
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const bool stream_w = tile.w <= 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KT = I / kBK;
+  const int k_start = ((nt % 2) * KT) / 2;
+  auto k_of = [&](int kt) { const int ks = kt + k_start; return ks >= KT ? ks - KT : ks; };
+  if (wave >= 8) {
+    // Loader l moves hh groups l + 4 i (i < G) and weight groups l + 4 j
+    // (j < 16) of every step; lane q fetches chunk swz(row, q & 7) of row
+    // 8 g + (q >> 3).  Buffer loads: a 32-bit per-lane byte offset and a
+    // scalar one.  hh is m-tile-blocked: K step k of row r at
+    // row0 * I + k * rows * 64 + r * 64.  A loader's weight groups are 32
+    // weight rows apart.
+    const int l = wave - 8, lr = lane >> 3, lc = lane & 7;
+    uint32_t voff_a[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int r = 8 * (l + 4 * i) + lr;   // rows past the tile: clamped, never stored
+      voff_a[i] = ((uint32_t)min(r, rows - 1) * kBK + swz(r, lc) * 8) * 2;
+    }
+    const int rb0 = 8 * l + lr;
+    const uint32_t voff_b = ((uint32_t)(nt * BN + rb0) * (uint32_t)I + swz(rb0, lc) * 8) * 2;
+    const uint32_t b_stride = 32u * (uint32_t)I * 2;
+    const uint32_t a_step = (uint32_t)rows * kBK * 2;
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(hh + (size_t)row0 * I), (short)0, 0x7fffffff, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + (size_t)e * H * I), (short)0, 0x7fffffff, kBufferFlags);
+    auto issue = [&](int kt, char* dst) {
+      const uint32_t k = (uint32_t)k_of(kt);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {   // weights first: the HBM wait
+        lds_void* d = (lds_void*)(dst + (NA + l + 4 * j) * 1024);
+        const uint32_t so = k * (kBK * 2) + (uint32_t)j * b_stride;
+        if (stream_w)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, d, 16, voff_b, so, 0, kCachePolicyNT);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, d, 16, voff_b, so, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(dst + (l + 4 * i) * 1024),
+                                                 16, voff_a[i], k * a_step, 0, 0);
+    };
+    issue(0, s0);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vmcnt<0>();   // step kt has landed (the only one in flight)
+      lds_barrier();     // publish it; the compute waves are done with step kt - 1
+      if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1 ? s1 : s0);
+    }
+    lds_barrier();       // the compute waves are done: the stages take the output
+    lds_barrier();       // ... which is now written
+  } else {
+    f32x4 acc[R][4];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int kt = 0; kt < KT; ++kt) {
+      lds_barrier();
+      const char* src = kt & 1 ? s1 : s0;
+      mma_step<R, 4, decltype(acc), NoHook, (G == 4)>(src, src + NA * 1024, 0, 64 * wave, lane,
+                                                       acc);
+    }
+    lds_barrier();       // every wave is done reading the stages
+    // rows [0, 64) through s0, [64, 128) through s1
+    const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      const Out out{rb < 4 ? s0 : s1};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          out.put((rb & 3) * 16 + 4 * q + i, 64 * wave + 16 * cb + c, acc[rb][cb][i]);
+    }
+    lds_barrier();
+  }
+  for (int j = threadIdx.x; j < rows * Out::kChunks; j += kW12Threads) {
+    const int r = j / Out::kChunks, cc = j - r * Out::kChunks;
+    const i32x4 v = *(const i32x4*)((r < 64 ? s0 : s1) + (r & 63) * Out::kPitch + cc * 16);
+    __builtin_nontemporal_store(v, (i32x4*)(C + (size_t)(row0 + r) * H + nt * BN + cc * 8));
+  }
+}
+
+// One block per (narrow m-tile, 512-row weight tile), XCD-aware as the other
+// GEMM kernels.  The narrow m-tiles are tiles[nwide[0] ..] (nnarrow[0] of
+// them); the grid is sized from the capacity bound (one per expert), surplus
+// blocks exit.
+__global__ __launch_bounds__(kW12Threads, 1) void ffn_down512_bf16(
+    const bf16* __restrict__ hh, const bf16* __restrict__ W, const int4* __restrict__ tiles,
+    const int* __restrict__ nwide, const int* __restrict__ nnarrow, int I, int H, int NT,
+    bf16* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char s0[kW12Stage];
+  __shared__ __attribute__((aligned(1024))) char s1[kW12Stage];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int mt = (slot / NT) * 8 + xcd;
+  const int nt = slot % NT;
+  if (mt >= *nnarrow) return;
+  const int4 tile = tiles[*nwide + mt];
+  switch ((tile.z + 31) >> 5) {
+    case 1: down512_item<1>(s0, s1, hh, W, tile, nt, I, H, C); break;
+    case 2: down512_item<2>(s0, s1, hh, W, tile, nt, I, H, C); break;
+    case 3: down512_item<3>(s0, s1, hh, W, tile, nt, I, H, C); break;
+    case 4: down512_item<4>(s0, s1, hh, W, tile, nt, I, H, C); break;
+    default: break;
+  }
+}
+
 // ------------------------------------------------------------ fp32 path --
 // Plain LDS-tiled FMA kernels for fp32 layers (exact fp32 products, fp32
 // accumulation); any H and I.  Tile: 32 rows x 32 outputs, K step 32.
@@ -970,9 +1130,18 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
   const bool dense = dense_shapes(dtype, H, I) && rows_per_expert >= kBmBf16 &&
                      (size_t)(gather ? gT : kBmBf16) * H < ((size_t)1 << 31) &&
                      (size_t)2 * I * H < ((size_t)1 << 31);
+  // Where the average FFN expert would have under 32 rows even if every
+  // pick went to one (decode), every tile is a single group: the 128-row
+  // tiles' deep rings stream the weights best, and neither the wide tiles
+  // nor the 512-row down tiles are used.  The 512-row kernel's buffer loads
+  // take 31-bit byte offsets within one expert's w2 and one m-tile's hh.
+  const bool enough_rows = (long long)rows_cap >= 32LL * n_ffn;
+  const bool down512 = dtype == MOE_BF16 && enough_rows && H % kW12BN == 0 &&
+                       (size_t)H * I * 2 < ((size_t)1 << 31);
   MOE_LAUNCH("ffn_tiles", s,
              ffn_tiles<<<1, 1024, 0, s>>>(offsets, n_ffn, bm, rows_cap, (int)mtmax, tiles,
-                                          ntiles, (int)fmax, dense ? full : nullptr, nfull));
+                                          ntiles, (int)fmax, dense ? full : nullptr, nfull,
+                                          down512 ? kW12MaxRows : 0));
   if (dtype == MOE_BF16) {
     // with the full m-tiles in the dense kernel, at most one m-tile per
     // expert is left for this one
@@ -1001,7 +1170,6 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
     // ones) 0.19 ms faster.  Where the average FFN expert would have under
     // 32 rows even if every pick went to one (decode), every tile is a
     // single group and the kernel without the wide path is launched.
-    const bool enough_rows = (long long)rows_cap >= 32LL * n_ffn;
     const bool wide_gu = enough_rows && (2 * I) % kBNGateUpWide == 0;
     const bool wide_dn = enough_rows && H % kBNWide == 0;
     const unsigned grid_gu = groups * 8 * nt1, grid_dn = groups * 8 * nt2;
@@ -1021,16 +1189,25 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
                                               (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2,
                                               full, nfull, I, I, H, H / kDenseBN,
                                               (bf16*)y_perm));
+    // the down GEMM's narrow m-tiles (at most 128 rows) in 512-row tiles;
+    // the main kernel takes the first part of tiles[] (ntiles[3] of them)
+    if (down512)
+      MOE_LAUNCH("ffn_down_narrow_bf16", s,
+                 ffn_down512_bf16<<<ceil_div(std::min(mtmax, (size_t)n_ffn), 8) * 8 *
+                                        (H / kW12BN),
+                                    kW12Threads, 0, s>>>(
+                     (const bf16*)hh, (const bf16*)w2, tiles, ntiles + 3, ntiles + 4, I, H,
+                     H / kW12BN, (bf16*)y_perm));
     if (wide_dn)
       MOE_LAUNCH("ffn_down_bf16", s,
                  ffn_mfma_bf16<false, kWideGroups><<<grid_dn, kGemmThreads, 0, s>>>(
-                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
-                     (bf16*)y_perm));
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles + 3, I, I, H,
+                     nt2, (bf16*)y_perm));
     else
       MOE_LAUNCH("ffn_down_bf16", s,
                  ffn_mfma_bf16<false, 0><<<grid_dn, kGemmThreads, 0, s>>>(
-                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles, I, I, H, nt2,
-                     (bf16*)y_perm));
+                     (const bf16*)hh, nullptr, 1, 1, (const bf16*)w2, tiles, ntiles + 3, I, I, H,
+                     nt2, (bf16*)y_perm));
   } else {
     dim3 g1(ceil_div(I, 32), (unsigned)mtmax), g2(ceil_div(H, 32), (unsigned)mtmax);
     MOE_LAUNCH("ffn_gateup_f32", s,
