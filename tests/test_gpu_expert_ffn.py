@@ -5,7 +5,8 @@ tiles and experts spanning several tiles.  Hidden sizes that are multiples of
 192 select the down GEMM's 192-row weight tiles for tiles of up to 224 rows
 (128-row ones for the rest); the others use 128-row tiles throughout.  At
 2I = 512 the gate/up GEMM's partial tiles of 2-5 groups take 256-row weight
-tiles."""
+tiles; where H is a multiple of 512 (H = 1024, 1536) the down GEMM's last
+m-tiles of up to 4 groups take 512-row weight tiles."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 ROWS = [1, 40, 70, 100, 150, 180, 200, 224, 230, 256, 300, 513, 17]
 
 
-@pytest.mark.parametrize("H,I", [(384, 128), (768, 256), (640, 192), (1024, 256)])
+@pytest.mark.parametrize("H,I", [(384, 128), (768, 256), (640, 192), (1024, 256), (1536, 256)])
 def test_expert_rows_match_oracle(H, I):
     dev = device()
     print(f"\n[case] expert FFN H={H} I={I} rows {ROWS}", flush=True)
