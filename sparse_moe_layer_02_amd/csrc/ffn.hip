@@ -180,6 +180,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // HBM again (measured: the weight loads alone took 575 us of a 1014 us gate/up
 // GEMM).
 constexpr int kCachePolicyNT = 2;
+// Buffer descriptor word 3 for raw 32-bit buffer loads on gfx9 parts (data
+// format 32, no swizzle, no index stride).
+constexpr int kBufferFlags = 0x00020000;
 
 template <int G, int BN = kBN>
 struct Ring {
@@ -370,7 +373,10 @@ struct NoHook {
 // (the dense kernel issues one of its next step's global->LDS loads there).
 // ONE_B: one set of B fragment registers, reloaded at the first group of the
 // second k block (one exposed LDS latency per step, 4 C fewer registers).
-template <int R, int C, class Acc, class Hook = NoHook, bool ONE_B = false>
+// SWAP: the B fragments feed the MFMA's first operand, so each 16 x 16 block
+// of acc holds the transposed product: lane (q = lane / 16, c = lane % 16)
+// gets B rows 4 q .. 4 q + 3 of the block against A row c.
+template <int R, int C, class Acc, class Hook = NoHook, bool ONE_B = false, bool SWAP = false>
 __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_row0, int b_row0,
                                          int lane, Acc& acc, const Hook& hook = Hook{}) {
   constexpr int kRG = R % 2 == 0 ? 2 : 1;   // row blocks per group
@@ -417,8 +423,11 @@ __device__ __forceinline__ void mma_step(const char* As, const char* Bs, int a_r
     for (int r = 0; r < kRG; ++r)
 #pragma unroll
       for (int cb = 0; cb < C; ++cb)
-        acc[rb0 + r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a[g & 1][r], b[ONE_B ? 0 : kk][cb], acc[rb0 + r][cb], 0, 0, 0);
+        acc[rb0 + r][cb] =
+            SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ONE_B ? 0 : kk][cb], a[g & 1][r],
+                                                           acc[rb0 + r][cb], 0, 0, 0)
+                 : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[g & 1][r], b[ONE_B ? 0 : kk][cb],
+                                                           acc[rb0 + r][cb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -696,29 +705,67 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 // tiles: half the activation bytes per flop of the 256 x 128 quadrant path.
 // On one 16,384-row expert the quadrant path's loads alone took 70 % of its
 // time and its MFMAs alone 50 % (timing-only builds); this kernel takes
-// ~0.80 ms for the gate/up GEMM against ~0.90 ms.
+// ~0.77 ms for the gate/up GEMM against ~0.90 ms.
 //   - 8 waves, 2 per SIMD; wave (wr, wc) = (w / 4, w % 4) computes rows
 //     [128 wr, +128) x weight rows [64 wc, +64) (128 accumulator registers);
 //   - no loader waves: each wave issues 8 of a K step's 64 global->LDS loads
-//     (A: 32 groups of 8 rows, B: 32 groups), 2 in each of the first four
-//     MFMA groups of the previous step;
-//   - two stages in two separately declared LDS arrays, loaded and read in
-//     turn: the compiler can tell that the loads into one do not touch the
-//     reads of the other, so no read waits for a load in flight (with one
-//     array it makes every fragment read wait for the wave's newest load);
+//     (A: 32 groups of 8 rows, B: 32 groups) among the MFMA groups of an
+//     earlier step, as buffer loads (32-bit per-lane offsets, the K step in
+//     the scalar offset);
+//   - activation tiles in a ring of three slots (loaded two steps ahead),
+//     weight tiles in a ring of two (one step ahead), five separately
+//     declared LDS arrays: the compiler can tell that the loads into one do
+//     not touch the reads of another, so no fragment read waits for a load
+//     in flight (with one array it made every read wait for the wave's
+//     newest load).  With two stages of both (every load one step ahead)
+//     the step-end wait for activation rows that missed L2 was exposed:
+//     skewed layer's full-tile gate/up 3.34 -> 3.19 ms with the deeper
+//     activation ring;
+//   - the output leaves straight from the accumulators, 16 bytes per lane
+//     (the MFMAs take the weight tile as their first operand, and the weight
+//     rows are ordered so that a lane holds 8 consecutive output columns);
 //   - measured and not kept: 32-wide K steps with four stages in four arrays
 //     (64-byte rows: 0.93 ms), super-items of 8 m-tiles x 4 weight tiles per
 //     XCD from k = 0 (heavy expert 0.78 ms, but the 64-expert layer's full
-//     tiles 20 % slower);
+//     tiles 20 % slower); the two waves of a SIMD issuing their loads in
+//     different MFMA groups (3-8 % slower); weight loads before activation
+//     loads with two stages (12 % slower);
 //   - gate/up pairing and the m-tile-blocked hh layout as in the other path;
 //     weights cached unless the expert has a single m-tile.
 constexpr int kDenseBN = 256;
-constexpr int kDenseStage = 72 * 1024;   // A 32 KB + B 32 KB of a K step; or half the output
-static_assert(128 * OutTile<kDenseBN>::kPitch <= kDenseStage, "half output tile fits a stage");
+constexpr int kDenseSlot = 32 * 1024;   // one operand tile of a K step: 256 rows x 128 B
+static_assert(5 * kDenseSlot <= kLdsBytes, "three A slots and two B slots");
+
+// Weight row held in row r of a dense tile (column tile nt).  Wave column wc
+// owns tile rows [64 wc, +64): 16-row blocks cb = 0..3, and after the
+// swapped MFMA a lane holds rows 4 q .. 4 q + 3 of each block.  Those rows
+// are ordered so that the lane's values are 8 consecutive output columns:
+//   gate/up: blocks 2p (gate) and 2p + 1 (up) of hh columns
+//     nt * 128 + 32 wc + 8 q + 4 p + i;
+//   down: block cb row 4 q + i is y column nt * 256 + 64 wc + 32 (cb / 2) +
+//     8 q + 4 (cb % 2) + i.
+__device__ __forceinline__ int dense_weight_row(bool gateup, int r, int nt, int I) {
+  const int wc = r >> 6, cb = (r >> 4) & 3, q = (r >> 2) & 3, i = r & 3;
+  if (gateup) {
+    const int j = nt * 128 + 32 * wc + 8 * q + 4 * (cb >> 1) + i;
+    return (cb & 1) ? I + j : j;
+  }
+  return nt * 256 + 64 * wc + 32 * (cb >> 1) + 8 * q + 4 * (cb & 1) + i;
+}
 
 // One (full m-tile, 256-row weight tile nt) item of the dense kernel.
+// LDS: the A tile of a K step (256 activation rows x 64 k, 32 KB) in a ring
+// of three slots, the B tile (256 weight rows) in a ring of two, five arrays
+// of 32 KB declared apart.  During step kt's MFMAs each wave issues its
+// share of step kt + 1's B tile (two loads in each of MFMA groups 0 and 1)
+// and of step kt + 2's A tile (one load in each of groups 2-5), and at the
+// end of the step waits for all but those last A loads.  The A tile, whose rows are token rows read by one m-tile's
+// column tiles at different K offsets and most often missed in L2, thus has
+// a step and a half to land; the B tile (the expert's weights, shared by
+// the m-tiles on the XCD and kept by the last-level cache) half a step.
 template <bool GATEUP>
-__device__ __forceinline__ void dense_item(char* s0, char* s1, const bf16* __restrict__ A,
+__device__ __forceinline__ void dense_item(char* a0, char* a1, char* a2, char* b0, char* b1,
+                                           const bf16* __restrict__ A,
                                            const int32_t* __restrict__ gather, int gK, int gT,
                                            const bf16* __restrict__ W, int4 tile, int nt,
                                            int KD, int I, int H, bf16* __restrict__ C) {
@@ -731,103 +778,135 @@ __device__ __forceinline__ void dense_item(char* s0, char* s1, const bf16* __res
   const int KT = KD / kBK;
   const int k_start = ((nt % 4) * KT) / 4;
   const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
-  const TileSrc t{gather ? A : A + (size_t)row0 * KD, gather ? gather + row0 : nullptr, gK, gT,
-                  BM, W + (size_t)e * wrows * KD, nt, I, GATEUP, stream_w,
-                  GATEUP ? KD : kBK, GATEUP ? kBK : BM * kBK};
+  const bf16* a_rows = gather ? A : A + (size_t)row0 * KD;
+  const int32_t* g = gather ? gather + row0 : nullptr;
+  const int a_pitch = GATEUP ? KD : kBK, a_step = GATEUP ? kBK : BM * kBK;
+  const bf16* w = W + (size_t)e * wrows * KD;
   // this wave's load groups: A and B groups wave + 8 i, i < 4; lane j of a
-  // group's load fetches chunk swz(row, j & 7) of row 8 g + (j >> 3).  Row
-  // offsets are 32-bit element offsets from the tile's bases (token rows of
-  // x, grouped rows or the m-tile's hh; one expert's weight rows).
+  // group's load fetches chunk swz(row, j & 7) of row 8 g + (j >> 3).  Buffer
+  // loads: a 32-bit per-lane byte offset from the tile's base (token rows of
+  // x, grouped rows or the m-tile's hh; one expert's weight rows) and a
+  // scalar one for the K step.
   const int lr = lane >> 3, lc = lane & 7;
   uint32_t aoff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (wave + 8 * i) * 8 + lr;
-    const int ar = t.gather ? min(max(t.gather[r], 0) / t.gK, t.gT - 1) : r;
-    aoff[i] = (uint32_t)ar * (uint32_t)t.a_pitch + swz(r, lc) * 8;
-    boff[i] = (uint32_t)weight_row<kDenseBN>(t, r) * (uint32_t)KD + swz(r, lc) * 8;
+    const int ar = g ? min(max(g[r], 0) / gK, gT - 1) : r;
+    aoff[i] = ((uint32_t)ar * (uint32_t)a_pitch + swz(r, lc) * 8) * 2;
+    boff[i] = ((uint32_t)dense_weight_row(GATEUP, r, nt, I) * (uint32_t)KD + swz(r, lc) * 8) * 2;
   }
-  auto k_of = [&](int kt) { const int ks = kt + k_start; return ks >= KT ? ks - KT : ks; };
-  // load u (0..7) of step kt into stage dst: A groups for u < 4, B after
-  auto load = [&](char* dst, int kt, int u) {
-    const int k = k_of(kt);
-    if (u < 4) {
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(t.a_rows + (size_t)k * t.a_step + aoff[u]),
-          (lds_void*)(dst + (wave + 8 * u) * 1024), 16, 0, 0);
-    } else {
-      const void* g = t.w + k * kBK + boff[u - 4];
-      lds_void* d = (lds_void*)(dst + 32768 + (wave + 8 * (u - 4)) * 1024);
-      if (stream_w)
-        __builtin_amdgcn_global_load_lds(g, d, 16, 0, kCachePolicyNT);
-      else
-        __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
-    }
+  const __amdgpu_buffer_rsrc_t rs_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_rows, (short)0, 0x7fffffff, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, 0x7fffffff, kBufferFlags);
+  // (kt < KT + 2: past the end it wraps into the sweep again)
+  auto k_of = [&](int kt) {
+    int ks = kt + k_start;
+    ks = ks >= KT ? ks - KT : ks;
+    return ks >= KT ? ks - KT : ks;
+  };
+  auto load_a = [&](char* dst, int kt, int u) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(dst + (wave + 8 * u) * 1024), 16,
+                                             aoff[u], (uint32_t)k_of(kt) * (a_step * 2), 0, 0);
+  };
+  auto load_b = [&](char* dst, int kt, int u) {
+    lds_void* d = (lds_void*)(dst + (wave + 8 * u) * 1024);
+    const uint32_t so = (uint32_t)k_of(kt) * (kBK * 2);
+    if (stream_w)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, d, 16, boff[u], so, 0, kCachePolicyNT);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, d, 16, boff[u], so, 0, 0);
   };
   f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-  // one K step from src while step kt_next (if any) loads into dst: two of
-  // this wave's loads in each of the first four MFMA groups, so that their
-  // issue overlaps matrix work and the last of them has half a step to land
-  auto step = [&](const char* src, char* dst, int kt_next) {
-    const bool more = kt_next < KT;
-    auto hook = [&](int g) {
-      if (more && g < 4) {
-        load(dst, kt_next, 2 * g);
-        load(dst, kt_next, 2 * g + 1);
+  // Every step issues the same loads -- past the end of the sweep they read
+  // real rows again into a slot no step reads -- so the wait count is one
+  // constant and the compiler's view of which slots have loads in flight
+  // is the same on every path.
+  auto step = [&](const char* as, const char* bs, char* bd, char* ad, int kt) {
+    auto hook = [&](int grp) {
+      if (grp < 2) {
+        load_b(bd, kt + 1, 2 * grp);
+        load_b(bd, kt + 1, 2 * grp + 1);
+      } else if (grp < 6) {
+        load_a(ad, kt + 2, grp - 2);
       }
     };
-    mma_step<8, 4, decltype(acc), decltype(hook), true>(src, src + 32768, 128 * wr, 64 * wc,
-                                                        lane, acc, hook);
-    wait_vmcnt<0>();   // this wave's loads of the next step have landed
-    lds_barrier();     // ... and everyone's; every wave is done with src
+    mma_step<8, 4, decltype(acc), decltype(hook), true, true>(as, bs, 128 * wr, 64 * wc, lane,
+                                                              acc, hook);
+    wait_vmcnt<4>();   // everything but step kt + 2's A loads has landed
+    lds_barrier();     // ... for every wave; every wave is done with as and bs
   };
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load(s0, 0, u);
-  wait_vmcnt<0>();
+  for (int u = 0; u < 4; ++u) load_a(a0, 0, u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_b(b0, 0, u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_a(a1, 1, u);
+  wait_vmcnt<4>();
   lds_barrier();
+  // step kt: A slot kt % 3, B slot kt % 2, six steps per pass.  The passes
+  // are straight-line code and the last steps nest, so that the compiler
+  // sees which slots can have loads in flight at every fragment read (with
+  // a guard on each step it assumed any step could be skipped and waited
+  // for every load before some of the reads).
   int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(s0, s1, kt + 1);
-    step(s1, s0, kt + 2);
+  for (; kt + 6 <= KT; kt += 6) {
+    step(a0, b0, b1, a2, kt);
+    step(a1, b1, b0, a0, kt + 1);
+    step(a2, b0, b1, a1, kt + 2);
+    step(a0, b1, b0, a2, kt + 3);
+    step(a1, b0, b1, a0, kt + 4);
+    step(a2, b1, b0, a1, kt + 5);
   }
-  if (kt < KT) step(s0, s1, KT);
-  // Epilogue: each half of the rows goes through its own stage buffer (waves
-  // wr = 0 through s0, wr = 1 through s1) and leaves 16 bytes per lane.
-  constexpr int NC = GATEUP ? kDenseBN / 2 : kDenseBN;
-  const OutTile<NC> out{wr == 0 ? s0 : s1};
-  const int c = lane & 15, q = lane >> 4;
-#pragma unroll
-  for (int rb = 0; rb < 8; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + 4 * q + i;   // row within the half
-      if (GATEUP) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          out.put(r, 32 * wc + 16 * p + c, silu_mul(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]));
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) out.put(r, 64 * wc + 16 * cb + c, acc[rb][cb][i]);
+  if (kt < KT) {
+    step(a0, b0, b1, a2, kt);
+    if (kt + 1 < KT) {
+      step(a1, b1, b0, a0, kt + 1);
+      if (kt + 2 < KT) {
+        step(a2, b0, b1, a1, kt + 2);
+        if (kt + 3 < KT) {
+          step(a0, b1, b0, a2, kt + 3);
+          if (kt + 4 < KT) step(a1, b0, b1, a0, kt + 4);
+        }
       }
     }
-  lds_barrier();
-  const int tid = threadIdx.x & 255;   // the four waves of this half
-  if (GATEUP) {
-    // hh, m-tile-blocked: 64-column block j of the m-tile's 256 rows at
-    // row0 * I + j * 256 * 64; this tile holds blocks 2 nt and 2 nt + 1
-    bf16* dst = C + (size_t)row0 * I;
-    for (int j = tid; j < 128 * OutTile<NC>::kChunks; j += 256) {
-      const int r = j / OutTile<NC>::kChunks, cc = j - r * OutTile<NC>::kChunks;
-      const i32x4 v = *(const i32x4*)(out.t + r * OutTile<NC>::kPitch + cc * 16);
-      bf16* blk = dst + (size_t)(nt * (NC / 64) + (cc >> 3)) * BM * 64;
-      __builtin_nontemporal_store(v, (i32x4*)(blk + (128 * wr + r) * 64 + (cc & 7) * 8));
+  }
+  wait_vmcnt<0>();   // the past-the-end loads land before the block's LDS is released
+  // Epilogue straight from the accumulators: lane holds m-tile row
+  // 128 wr + 16 rb + c and 8 consecutive output columns per store.
+  const int c = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) {
+    const int r = 128 * wr + 16 * rb + c;
+    if (GATEUP) {
+      // hh, m-tile-blocked: 64-column block j of the m-tile's 256 rows at
+      // row0 * I + j * 256 * 64
+      const int col = nt * 128 + 32 * wc + 8 * q;
+      bf16x8 v;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[4 * p + i] = (bf16)silu_mul(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]);
+      __builtin_nontemporal_store(
+          v, (bf16x8*)(C + (size_t)row0 * I + (size_t)(col >> 6) * BM * 64 + r * 64 + (col & 63)));
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int col = nt * 256 + 64 * wc + 32 * p + 8 * q;
+        bf16x8 v;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * h + i] = (bf16)acc[rb][2 * p + h][i];
+        __builtin_nontemporal_store(v, (bf16x8*)(C + (size_t)(row0 + r) * H + col));
+      }
     }
-  } else {
-    out.flush(C + (size_t)(row0 + 128 * wr) * H + nt * NC, H, 128, tid);
   }
 }
 
@@ -840,14 +919,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_dense_bf16(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
     const bf16* __restrict__ W, const int4* __restrict__ full, const int* __restrict__ nfull,
     int KD, int I, int H, int NT, bf16* __restrict__ C) {
-  __shared__ __attribute__((aligned(1024))) char s0[kDenseStage];
-  __shared__ __attribute__((aligned(1024))) char s1[kDenseStage];
+  __shared__ __attribute__((aligned(1024))) char a0[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char a1[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char a2[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char b0[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char b1[kDenseSlot];
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int mt = (slot / NT) * 8 + xcd;
   const int nt = slot % NT;
   if (mt >= nfull[0]) return;
-  dense_item<GATEUP>(s0, s1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
+  dense_item<GATEUP>(a0, a1, a2, b0, b1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
 }
 
 // ----------------------- down GEMM: 512-row weight tiles, at most 128 rows --
@@ -870,9 +952,6 @@ constexpr int kW12Threads = 768;
 constexpr int kW12BN = 512;
 constexpr int kW12Stage = 80 * 1024;
 constexpr int kW12MaxRows = 128;
-// Buffer descriptor word 3 for raw 32-bit buffer loads on gfx9 parts (data
-// format 32, no swizzle, no index stride).
-constexpr int kBufferFlags = 0x00020000;
 static_assert(64 * OutTile<kW12BN>::kPitch <= kW12Stage, "half the output tile fits a stage");
 
 template <int G>
@@ -1125,11 +1204,11 @@ hipError_t launch_expert_ffn(const void* x_perm, const int32_t* gather, int gK, 
   // An expert holds at most one row per token: the gather path knows the
   // tokens, so a batch of fewer than 256 tokens has no full m-tile.
   const int rows_per_expert = gather ? min(rows_cap, gT) : rows_cap;
-  // (and the dense kernel's 32-bit row offsets must fit: token rows of x and
-  // weight rows of one expert)
+  // (and the dense kernel's 31-bit buffer byte offsets must reach: token
+  // rows of x and the weights of one expert)
   const bool dense = dense_shapes(dtype, H, I) && rows_per_expert >= kBmBf16 &&
-                     (size_t)(gather ? gT : kBmBf16) * H < ((size_t)1 << 31) &&
-                     (size_t)2 * I * H < ((size_t)1 << 31);
+                     (size_t)(gather ? gT : kBmBf16) * H * 2 < ((size_t)1 << 31) &&
+                     (size_t)2 * I * H * 2 < ((size_t)1 << 31);
   // Where the average FFN expert would have under 32 rows even if every
   // pick went to one (decode), every tile is a single group: the 128-row
   // tiles' deep rings stream the weights best, and neither the wide tiles
