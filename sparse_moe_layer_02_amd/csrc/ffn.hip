@@ -759,10 +759,11 @@ __device__ __forceinline__ int dense_weight_row(bool gateup, int r, int nt, int 
 // of 32 KB declared apart.  During step kt's MFMAs each wave issues its
 // share of step kt + 1's B tile (two loads in each of MFMA groups 0 and 1)
 // and of step kt + 2's A tile (one load in each of groups 2-5), and at the
-// end of the step waits for all but those last A loads.  The A tile, whose rows are token rows read by one m-tile's
-// column tiles at different K offsets and most often missed in L2, thus has
-// a step and a half to land; the B tile (the expert's weights, shared by
-// the m-tiles on the XCD and kept by the last-level cache) half a step.
+// end of the step waits for all but those last A loads.  The A tile, whose
+// rows are token rows read by one m-tile's column tiles at different K
+// offsets and most often missed in L2, thus has more than a step to land;
+// the B tile (the expert's weights, shared by the m-tiles on the XCD and
+// kept by the last-level cache) most of one.
 template <bool GATEUP>
 __device__ __forceinline__ void dense_item(char* a0, char* a1, char* a2, char* b0, char* b1,
                                            const bf16* __restrict__ A,
