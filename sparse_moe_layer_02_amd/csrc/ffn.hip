@@ -705,22 +705,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 // tiles: half the activation bytes per flop of the 256 x 128 quadrant path.
 // On one 16,384-row expert the quadrant path's loads alone took 70 % of its
 // time and its MFMAs alone 50 % (timing-only builds); this kernel takes
-// ~0.77 ms for the gate/up GEMM against ~0.90 ms.
+// ~0.75 ms for the gate/up GEMM against ~0.90 ms.
 //   - 8 waves, 2 per SIMD; wave (wr, wc) = (w / 4, w % 4) computes rows
 //     [128 wr, +128) x weight rows [64 wc, +64) (128 accumulator registers);
 //   - no loader waves: each wave issues 8 of a K step's 64 global->LDS loads
 //     (A: 32 groups of 8 rows, B: 32 groups) among the MFMA groups of an
 //     earlier step, as buffer loads (32-bit per-lane offsets, the K step in
 //     the scalar offset);
-//   - activation tiles in a ring of three slots (loaded two steps ahead),
-//     weight tiles in a ring of two (one step ahead), five separately
+//   - weight tiles in a ring of three slots (loaded two steps ahead),
+//     activation tiles in a ring of two (one step ahead), five separately
 //     declared LDS arrays: the compiler can tell that the loads into one do
 //     not touch the reads of another, so no fragment read waits for a load
 //     in flight (with one array it made every read wait for the wave's
 //     newest load).  With two stages of both (every load one step ahead)
-//     the step-end wait for activation rows that missed L2 was exposed:
-//     skewed layer's full-tile gate/up 3.34 -> 3.19 ms with the deeper
-//     activation ring;
+//     the step-end wait was exposed.  Measured on the skewed layer (full
+//     tiles, same box): gate/up 3.34 ms with two stages of both, 3.13-3.16
+//     with the activation tiles two steps ahead, 3.03 with the weight tiles
+//     two steps ahead and the cache-policy branch gone (below); down 1.75 ->
+//     1.67-1.69 ms;
 //   - the output leaves straight from the accumulators, 16 bytes per lane
 //     (the MFMAs take the weight tile as their first operand, and the weight
 //     rows are ordered so that a lane holds 8 consecutive output columns);
@@ -731,7 +733,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mfma_bf16(
 //     different MFMA groups (3-8 % slower); weight loads before activation
 //     loads with two stages (12 % slower);
 //   - gate/up pairing and the m-tile-blocked hh layout as in the other path;
-//     weights cached unless the expert has a single m-tile.
+//     weights always loaded with the default cache policy (the expert's
+//     other m-tiles read them again; a choice per block made the compiler
+//     lose track of which slots had loads in flight).
 constexpr int kDenseBN = 256;
 constexpr int kDenseSlot = 32 * 1024;   // one operand tile of a K step: 256 rows x 128 B
 static_assert(5 * kDenseSlot <= kLdsBytes, "three A slots and two B slots");
@@ -754,24 +758,21 @@ __device__ __forceinline__ int dense_weight_row(bool gateup, int r, int nt, int 
 }
 
 // One (full m-tile, 256-row weight tile nt) item of the dense kernel.
-// LDS: the A tile of a K step (256 activation rows x 64 k, 32 KB) in a ring
-// of three slots, the B tile (256 weight rows) in a ring of two, five arrays
-// of 32 KB declared apart.  During step kt's MFMAs each wave issues its
-// share of step kt + 1's B tile (two loads in each of MFMA groups 0 and 1)
-// and of step kt + 2's A tile (one load in each of groups 2-5), and at the
-// end of the step waits for all but those last A loads.  The A tile, whose
-// rows are token rows read by one m-tile's column tiles at different K
-// offsets and most often missed in L2, thus has more than a step to land;
-// the B tile (the expert's weights, shared by the m-tiles on the XCD and
-// kept by the last-level cache) most of one.
+// LDS: the weight tile of a K step (256 weight rows x 64 k, 32 KB) in a ring
+// of three slots w0-w2, the activation tile (256 rows) in a ring of two,
+// a0-a1, five arrays of 32 KB declared apart.  During step kt's MFMAs each
+// wave issues its share of step kt + 1's activation tile (two loads in each
+// of MFMA groups 0 and 1) and of step kt + 2's weight tile (one load in each
+// of groups 2-5), and at the end of the step waits for all but those last
+// weight loads: the weights have more than a step to land, the activation
+// rows most of one.
 template <bool GATEUP>
-__device__ __forceinline__ void dense_item(char* a0, char* a1, char* a2, char* b0, char* b1,
+__device__ __forceinline__ void dense_item(char* w0, char* w1, char* w2, char* a0, char* a1,
                                            const bf16* __restrict__ A,
                                            const int32_t* __restrict__ gather, int gK, int gT,
                                            const bf16* __restrict__ W, int4 tile, int nt,
                                            int KD, int I, int H, bf16* __restrict__ C) {
   const int e = tile.x, row0 = tile.y;
-  const bool stream_w = tile.w <= 1;
   constexpr int BM = kBmBf16;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -812,12 +813,8 @@ __device__ __forceinline__ void dense_item(char* a0, char* a1, char* a2, char* b
                                              aoff[u], (uint32_t)k_of(kt) * (a_step * 2), 0, 0);
   };
   auto load_b = [&](char* dst, int kt, int u) {
-    lds_void* d = (lds_void*)(dst + (wave + 8 * u) * 1024);
-    const uint32_t so = (uint32_t)k_of(kt) * (kBK * 2);
-    if (stream_w)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, d, 16, boff[u], so, 0, kCachePolicyNT);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, d, 16, boff[u], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(dst + (wave + 8 * u) * 1024), 16,
+                                             boff[u], (uint32_t)k_of(kt) * (kBK * 2), 0, 0);
   };
   f32x4 acc[8][4];
 #pragma unroll
@@ -828,51 +825,53 @@ __device__ __forceinline__ void dense_item(char* a0, char* a1, char* a2, char* b
   // real rows again into a slot no step reads -- so the wait count is one
   // constant and the compiler's view of which slots have loads in flight
   // is the same on every path.
-  auto step = [&](const char* as, const char* bs, char* bd, char* ad, int kt) {
+  // step kt reads weight slot kt % 3 and activation slot kt % 2
+  auto step = [&](const char* ws, const char* as, char* ad, char* wd, int kt) {
     auto hook = [&](int grp) {
       if (grp < 2) {
-        load_b(bd, kt + 1, 2 * grp);
-        load_b(bd, kt + 1, 2 * grp + 1);
+        load_a(ad, kt + 1, 2 * grp);
+        load_a(ad, kt + 1, 2 * grp + 1);
       } else if (grp < 6) {
-        load_a(ad, kt + 2, grp - 2);
+        load_b(wd, kt + 2, grp - 2);
       }
     };
-    mma_step<8, 4, decltype(acc), decltype(hook), true, true>(as, bs, 128 * wr, 64 * wc, lane,
+    mma_step<8, 4, decltype(acc), decltype(hook), true, true>(as, ws, 128 * wr, 64 * wc, lane,
                                                               acc, hook);
-    wait_vmcnt<4>();   // everything but step kt + 2's A loads has landed
-    lds_barrier();     // ... for every wave; every wave is done with as and bs
+    wait_vmcnt<4>();   // everything but step kt + 2's weight loads has landed
+    lds_barrier();     // ... for every wave; every wave is done with ws and as
   };
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_b(w0, 0, u);
 #pragma unroll
   for (int u = 0; u < 4; ++u) load_a(a0, 0, u);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) load_b(b0, 0, u);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) load_a(a1, 1, u);
+  for (int u = 0; u < 4; ++u) load_b(w1, 1, u);
   wait_vmcnt<4>();
   lds_barrier();
-  // step kt: A slot kt % 3, B slot kt % 2, six steps per pass.  The passes
-  // are straight-line code and the last steps nest, so that the compiler
-  // sees which slots can have loads in flight at every fragment read (with
-  // a guard on each step it assumed any step could be skipped and waited
-  // for every load before some of the reads).
+  // Six steps per pass.  The passes are straight-line code and the last
+  // steps nest, so that the compiler sees which slots can have loads in
+  // flight at every fragment read (with a guard on each step it assumed any
+  // step could be skipped, and with a branch between two cache policies in
+  // the loads it merged the two paths' views; either way it waited for every
+  // load before some of the reads).
   int kt = 0;
   for (; kt + 6 <= KT; kt += 6) {
-    step(a0, b0, b1, a2, kt);
-    step(a1, b1, b0, a0, kt + 1);
-    step(a2, b0, b1, a1, kt + 2);
-    step(a0, b1, b0, a2, kt + 3);
-    step(a1, b0, b1, a0, kt + 4);
-    step(a2, b1, b0, a1, kt + 5);
+    step(w0, a0, a1, w2, kt);
+    step(w1, a1, a0, w0, kt + 1);
+    step(w2, a0, a1, w1, kt + 2);
+    step(w0, a1, a0, w2, kt + 3);
+    step(w1, a0, a1, w0, kt + 4);
+    step(w2, a1, a0, w1, kt + 5);
   }
   if (kt < KT) {
-    step(a0, b0, b1, a2, kt);
+    step(w0, a0, a1, w2, kt);
     if (kt + 1 < KT) {
-      step(a1, b1, b0, a0, kt + 1);
+      step(w1, a1, a0, w0, kt + 1);
       if (kt + 2 < KT) {
-        step(a2, b0, b1, a1, kt + 2);
+        step(w2, a0, a1, w1, kt + 2);
         if (kt + 3 < KT) {
-          step(a0, b1, b0, a2, kt + 3);
-          if (kt + 4 < KT) step(a1, b0, b1, a0, kt + 4);
+          step(w0, a1, a0, w2, kt + 3);
+          if (kt + 4 < KT) step(w1, a0, a1, w0, kt + 4);
         }
       }
     }
@@ -920,17 +919,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_dense_bf16(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, int gK, int gT,
     const bf16* __restrict__ W, const int4* __restrict__ full, const int* __restrict__ nfull,
     int KD, int I, int H, int NT, bf16* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char w0[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char w1[kDenseSlot];
+  __shared__ __attribute__((aligned(1024))) char w2[kDenseSlot];
   __shared__ __attribute__((aligned(1024))) char a0[kDenseSlot];
   __shared__ __attribute__((aligned(1024))) char a1[kDenseSlot];
-  __shared__ __attribute__((aligned(1024))) char a2[kDenseSlot];
-  __shared__ __attribute__((aligned(1024))) char b0[kDenseSlot];
-  __shared__ __attribute__((aligned(1024))) char b1[kDenseSlot];
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int mt = (slot / NT) * 8 + xcd;
   const int nt = slot % NT;
   if (mt >= nfull[0]) return;
-  dense_item<GATEUP>(a0, a1, a2, b0, b1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
+  dense_item<GATEUP>(w0, w1, w2, a0, a1, A, gather, gK, gT, W, full[mt], nt, KD, I, H, C);
 }
 
 // ----------------------- down GEMM: 512-row weight tiles, at most 128 rows --
