@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void sim_mean(const double* __restrict__ part_
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0) *mean = E > 1 ? (float)(red[0] / ((double)E * (double)(E - 1))) : 0.f;
