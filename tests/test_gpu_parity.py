@@ -101,6 +101,20 @@ def test_multi_tile_experts_bf16():
     _e2e(cfg, inp, buf)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+def test_multi_tile_experts_full_tile_kernel_bf16(path):
+    # hidden 512 and intermediate 256 are shapes the full-tile kernel takes:
+    # ~660 rows per FFN expert give two full 256-row m-tiles (K sweeps of 8
+    # steps for gate/up, 4 for down: one six-step pass plus a tail, and a
+    # tail alone) and a ragged partial one, through both dispatch paths
+    cfg = workload.MoEConfig("multitile_full", T=2000, H=512, N=4, Z=2, I=256, K=2, dtype="bf16",
+                             sigma_w=0.05, bias_lo=-0.01, bias_hi=0.01, scale=1.0)
+    inp, buf = _run(cfg, path=path)
+    assert host(buf["counts"])[:cfg.N].max() > 512
+    stage_checks(cfg, inp, buf)
+    _e2e(cfg, inp, buf)
+
+
 def test_k_equals_e_picks_every_expert():
     cfg = workload.MoEConfig("k_eq_e", T=70, H=128, N=5, Z=3, I=64, K=8, dtype="bf16",
                              sigma_w=0.05, bias_lo=-0.1, bias_hi=0.1, scale=1.0)
