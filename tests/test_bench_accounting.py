@@ -89,3 +89,20 @@ def test_stored_traffic_is_used_only_for_its_source_and_workload(tmp_path, monke
     assert bench.measured_traffic("prefill_bf16") == 123
     src.write_text("__global__ void k() { return; }\n")
     assert bench.measured_traffic("prefill_bf16") is None
+
+
+def test_call_floors_of_the_prefill_layer():
+    cfg, counts, S = _prefill_counts()
+    names = [n for ns in bench.CALLS.values() for n in ns]
+    kern = {n: (1, 1.0) for n in names}          # every kernel: one launch of 1 ms
+    calls = bench.call_floors(cfg, counts, S, kern)
+    T, H, E, K = cfg.T, cfg.H, cfg.E, cfg.K
+    r = calls["moe_router_logits"]
+    assert r["bytes"] == T * H * 2 + E * H * 4 + T * E * 4 == 144703488
+    assert r["gflop"] == pytest.approx(3 * 2 * T * E * H / 1e9, abs=0.01)   # three bf16 passes
+    assert r["floor_us"] == pytest.approx(3 * 2 * T * E * H / 2.5e15 * 1e6, abs=0.1)
+    f = calls["moe_expert_ffn_gather"]                  # no grouped copy: the gather call
+    assert f["bytes"] == 26837516288 + 13952614400
+    assert f["floor_us"] == pytest.approx((26837516288 + 13952614400) / 8e12 * 1e6, abs=0.1)
+    c = calls["moe_combine_identity"]
+    assert c["bytes"] == S * H * 2 + 2 * T * H * 2 + T * K * 8
