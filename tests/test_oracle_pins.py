@@ -275,6 +275,38 @@ def test_layer_matches_brute_force(seed, s):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
 
 
+def _swept_shapes(n=16, seed=11):
+    """Random small pools: T, H, N (0 allowed), Z (0 allowed), I, K (up to
+    E), compensation scale; a fixed list, so a failure names its case."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N, Z = int(r.integers(0, 9)), int(r.integers(0, 6))
+        if N + Z == 0:
+            continue
+        out.append(dict(seed=int(r.integers(0, 10**6)), T=int(r.integers(1, 40)),
+                        H=int(r.integers(1, 24)), N=N, Z=Z, I=int(r.integers(1, 10)),
+                        K=int(r.integers(1, N + Z + 1)), s=float(np.round(r.uniform(0.1, 3.0), 3))))
+    return out
+
+
+@pytest.mark.parametrize("c", _swept_shapes(),
+                         ids=lambda c: "T{T}-H{H}-N{N}-Z{Z}-I{I}-K{K}".format(**c))
+def test_layer_matches_brute_force_on_swept_shapes(c):
+    # Technical Report notes, Key claims [§2.1, §2.3.2]: the layer output is
+    # the gate-weighted sum over the kept experts of the pool, FFN outputs
+    # scaled by the compensation factor; brute force loops over the whole
+    # pool with weight 0 for the experts a token does not keep.
+    x, wr, b, w13, w2, K = _tiny(c["seed"], T=c["T"], H=c["H"], N=c["N"], Z=c["Z"], I=c["I"],
+                                 K=c["K"])
+    got = oracle.layer(x, wr, b, w13, w2, K, c["s"])
+    ref = _brute_force(x, wr, b, w13, w2, K, c["s"])
+    np.testing.assert_allclose(got["y"], ref, rtol=0, atol=1e-12 * max(np.abs(ref).max(), 1e-30))
+    # counts sum to T*K over the pool, and the FFN rows are the FFN picks
+    assert int(got["counts"].sum()) == c["T"] * K
+    assert int(got["offsets"][-1]) == int((got["idx"] < c["N"]).sum())
+
+
 def test_layer_with_routing_on_the_oracles_own_choice_is_the_layer():
     # the flip-rule reference row, fed the choice the oracle made itself,
     # must be the oracle's layer output bit for bit
