@@ -16,6 +16,8 @@
  *     never allocates, frees or keeps a pointer after the call returns.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *     void*, NULL = the default stream) and returns without synchronising.
+ *     The calling thread's current HIP device must be the one the pointers
+ *     and the stream belong to.
  *     Calls on one stream may follow each other with no host round trip:
  *     data-dependent sizes (rows per expert) stay on the device.
  *   - Arguments are validated on the host BEFORE any HIP call; a failed check

@@ -2,7 +2,8 @@
 
 Argument marshalling only: each function below has the name of the C entry
 point it calls, checks dtypes/devices/shapes of the torch tensors it is given,
-and passes their device pointers plus the current HIP stream.  Every step of
+and passes their device pointers plus the current HIP stream of their device,
+with that device made current for the call.  Every step of
 the layer runs in the library's HIP kernels; there is no CPU or PyTorch
 fallback -- if the shared library is missing, importing a function raises.
 
@@ -124,7 +125,7 @@ def moe_router_logits(x, w_router, logits, w_planes=None):
     """logits[T, E] (fp32) = x[T, H] @ w_router[E, H]^T.  w_planes: the
     router weights' bf16 planes from moe_router_split_weights (bitwise the
     same logits, without the split inside the large-batch kernel)."""
-    _dev(x, w_router, logits, w_planes)
+    d = _dev(x, w_router, logits, w_planes)
     _want(w_router, torch.float32, "w_router")
     _want(logits, torch.float32, "logits")
     T, H = x.shape
@@ -132,27 +133,30 @@ def moe_router_logits(x, w_router, logits, w_planes=None):
     _require(w_router.shape == (E, H) and logits.shape == (T, E),
              "w_router.shape == (E, H) and logits.shape == (T, E)")
     if w_planes is None:
-        _check("moe_router_logits", lib().moe_router_logits(
-            _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
+        with torch.cuda.device(d):
+            _check("moe_router_logits", lib().moe_router_logits(
+                _ptr(x), _DT[x.dtype], _ptr(w_router), T, H, E, _ptr(logits), _stream(x)))
         return
     _want(w_planes, torch.bfloat16, "w_planes")
     _require(w_planes.shape == (3, E, H), "w_planes.shape == (3, E, H)")
-    _check("moe_router_logits_planes", lib().moe_router_logits_planes(
-        _ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(w_planes), T, H, E, _ptr(logits),
-        _stream(x)))
+    with torch.cuda.device(d):
+        _check("moe_router_logits_planes", lib().moe_router_logits_planes(
+            _ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(w_planes), T, H, E, _ptr(logits),
+            _stream(x)))
 
 
 def moe_router_split_weights(w_router, w_planes):
     """w_planes[3, E, H] (bf16) = the exact split w = hi + mid + lo of the fp32
     router weights (a weight-format preparation; redo it when w_router
     changes)."""
-    _dev(w_router, w_planes)
+    d = _dev(w_router, w_planes)
     _want(w_router, torch.float32, "w_router")
     _want(w_planes, torch.bfloat16, "w_planes")
     E, H = w_router.shape
     _require(w_planes.shape == (3, E, H), "w_planes.shape == (3, E, H)")
-    _check("moe_router_split_weights", lib().moe_router_split_weights(
-        _ptr(w_router), E, H, _ptr(w_planes), _stream(w_router)))
+    with torch.cuda.device(d):
+        _check("moe_router_split_weights", lib().moe_router_split_weights(
+            _ptr(w_router), E, H, _ptr(w_planes), _stream(w_router)))
 
 
 def prepare_router(w_router, buf):
@@ -169,7 +173,7 @@ def prepare_router(w_router, buf):
 
 def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
     """Top-K of logits + bias (lower id on ties), softmax gates, histogram."""
-    _dev(logits, bias, topk_idx, topk_gate, counts, dev_status)
+    d = _dev(logits, bias, topk_idx, topk_gate, counts, dev_status)
     T, E = logits.shape
     _want(logits, torch.float32, "logits")
     _want(bias, torch.float32, "bias")
@@ -179,9 +183,10 @@ def moe_route(logits, bias, K, topk_idx, topk_gate, counts, dev_status=None):
     _require(bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K),
              "bias.shape == (E,) and topk_idx.shape == (T, K) and topk_gate.shape == (T, K)")
     _require(counts.shape == (E,), "counts.shape == (E,)")
-    _check("moe_route", lib().moe_route(
-        _ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
-        _ptr(dev_status), _stream(logits)))
+    with torch.cuda.device(d):
+        _check("moe_route", lib().moe_route(
+            _ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+            _ptr(dev_status), _stream(logits)))
 
 
 def moe_permute(x, topk_idx, counts, n_ffn, offsets, x_perm, row_src, slot_row):
@@ -189,7 +194,7 @@ def moe_permute(x, topk_idx, counts, n_ffn, offsets, x_perm, row_src, slot_row):
     is moe_route's histogram of topk_idx.  With x_perm None only the indices
     are written (for moe_expert_ffn_gather); x still gives T, H and the
     dtype."""
-    _dev(x, topk_idx, counts, offsets, x_perm, row_src, slot_row)
+    d = _dev(x, topk_idx, counts, offsets, x_perm, row_src, slot_row)
     for t, n in ((topk_idx, "topk_idx"), (counts, "counts"), (offsets, "offsets"),
                  (row_src, "row_src"), (slot_row, "slot_row")):
         _want(t, torch.int32, n)
@@ -202,10 +207,11 @@ def moe_permute(x, topk_idx, counts, n_ffn, offsets, x_perm, row_src, slot_row):
     if x_perm is not None:
         _require(x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K,
                  "x_perm.dtype == x.dtype and x_perm.shape[1] == H and x_perm.shape[0] >= T * K")
-    _check("moe_permute", lib().moe_permute(
-        _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), _ptr(counts),
-        T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row),
-        _stream(topk_idx)))
+    with torch.cuda.device(d):
+        _check("moe_permute", lib().moe_permute(
+            _ptr(x) if x_perm is not None else None, _DT[x.dtype], _ptr(topk_idx), _ptr(counts),
+            T, H, K, n_ffn, _ptr(offsets), _ptr(x_perm), _ptr(row_src), _ptr(slot_row),
+            _stream(topk_idx)))
 
 
 def moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype):
@@ -214,7 +220,7 @@ def moe_expert_ffn_workspace_bytes(rows_cap, n_ffn, I, dtype):
 
 def moe_expert_ffn(x_perm, offsets, w13, w2, y_perm, ws):
     """SwiGLU experts on the grouped rows; empty experts skipped."""
-    _dev(x_perm, offsets, w13, w2, y_perm, ws)
+    d = _dev(x_perm, offsets, w13, w2, y_perm, ws)
     rows_cap, H = x_perm.shape
     N, I2, H2 = w13.shape
     I = I2 // 2
@@ -222,14 +228,15 @@ def moe_expert_ffn(x_perm, offsets, w13, w2, y_perm, ws):
              "H2 == H and w2.shape == (N, H, I) and y_perm.shape == x_perm.shape")
     _require(w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype,
              "w13.dtype == w2.dtype == x_perm.dtype == y_perm.dtype")
-    _check("moe_expert_ffn", lib().moe_expert_ffn(
-        _ptr(x_perm), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2), _DT[x_perm.dtype],
-        _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x_perm)))
+    with torch.cuda.device(d):
+        _check("moe_expert_ffn", lib().moe_expert_ffn(
+            _ptr(x_perm), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2), _DT[x_perm.dtype],
+            _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x_perm)))
 
 
 def moe_expert_ffn_gather(x, K, row_src, offsets, w13, w2, y_perm, ws):
     """moe_expert_ffn reading row r's activations from x[row_src[r] // K]."""
-    _dev(x, row_src, offsets, w13, w2, y_perm, ws)
+    d = _dev(x, row_src, offsets, w13, w2, y_perm, ws)
     _want(row_src, torch.int32, "row_src")
     T, H = x.shape
     rows_cap = y_perm.shape[0]
@@ -240,9 +247,10 @@ def moe_expert_ffn_gather(x, K, row_src, offsets, w13, w2, y_perm, ws):
     _require(row_src.numel() >= rows_cap, "row_src.numel() >= rows_cap")
     _require(w13.dtype == w2.dtype == x.dtype == y_perm.dtype,
              "w13.dtype == w2.dtype == x.dtype == y_perm.dtype")
-    _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
-        _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
-        _DT[x.dtype], _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    with torch.cuda.device(d):
+        _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
+            _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
+            _DT[x.dtype], _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_EXPERT_FFN_NOALLOC_SCRATCH_BYTES
@@ -252,7 +260,7 @@ def moe_expert_ffn_gather_noalloc(x, K, row_src, offsets, w13, w2, y_perm):
     """moe_expert_ffn_gather with its workspace in the library's fixed
     per-GPU scratch (no allocation; for callers that cannot allocate).
     Calls that overlap on one GPU race; order them on one stream."""
-    _dev(x, row_src, offsets, w13, w2, y_perm)
+    d = _dev(x, row_src, offsets, w13, w2, y_perm)
     _want(row_src, torch.int32, "row_src")
     T, H = x.shape
     rows_cap = y_perm.shape[0]
@@ -263,14 +271,15 @@ def moe_expert_ffn_gather_noalloc(x, K, row_src, offsets, w13, w2, y_perm):
     _require(row_src.numel() >= rows_cap, "row_src.numel() >= rows_cap")
     _require(w13.dtype == w2.dtype == x.dtype == y_perm.dtype,
              "w13.dtype == w2.dtype == x.dtype == y_perm.dtype")
-    _check("moe_expert_ffn_gather_noalloc", lib().moe_expert_ffn_gather_noalloc(
-        _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
-        _DT[x.dtype], _ptr(y_perm), _stream(x)))
+    with torch.cuda.device(d):
+        _check("moe_expert_ffn_gather_noalloc", lib().moe_expert_ffn_gather_noalloc(
+            _ptr(x), T, K, _ptr(row_src), _ptr(offsets), rows_cap, N, H, I, _ptr(w13), _ptr(w2),
+            _DT[x.dtype], _ptr(y_perm), _stream(x)))
 
 
 def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
     """y_acc = (sum of identity-expert gates) * x, fp32."""
-    _dev(x, topk_idx, topk_gate, y_acc)
+    d = _dev(x, topk_idx, topk_gate, y_acc)
     T, H = x.shape
     K = topk_idx.shape[1]
     _want(topk_idx, torch.int32, "topk_idx")
@@ -278,9 +287,10 @@ def moe_zero_experts(x, topk_idx, topk_gate, n_ffn, y_acc):
     _want(y_acc, torch.float32, "y_acc")
     _require(topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H),
              "topk_idx.shape == (T, K) and topk_gate.shape == (T, K) and y_acc.shape == (T, H)")
-    _check("moe_zero_experts", lib().moe_zero_experts(
-        _ptr(x), _DT[x.dtype], _ptr(topk_idx), _ptr(topk_gate), T, H, K, n_ffn, _ptr(y_acc),
-        _stream(x)))
+    with torch.cuda.device(d):
+        _check("moe_zero_experts", lib().moe_zero_experts(
+            _ptr(x), _DT[x.dtype], _ptr(topk_idx), _ptr(topk_gate), T, H, K, n_ffn, _ptr(y_acc),
+            _stream(x)))
 
 
 def _combine_args(y_perm, slot_row, topk_gate, y):
@@ -299,29 +309,31 @@ def _combine_args(y_perm, slot_row, topk_gate, y):
 
 def moe_combine(y_perm, slot_row, topk_gate, ffn_scale, y_acc, y):
     """y = y_acc + sum of ffn_scale * gate * y_perm rows, in slot order."""
-    _dev(y_perm, slot_row, topk_gate, y_acc, y)
+    d = _dev(y_perm, slot_row, topk_gate, y_acc, y)
     T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
     _want(y_acc, torch.float32, "y_acc")
     _require(y_acc.shape == (T, H), "y_acc.shape == (T, H)")
-    _check("moe_combine", lib().moe_combine(
-        _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
-        _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
+    with torch.cuda.device(d):
+        _check("moe_combine", lib().moe_combine(
+            _ptr(y_perm), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
+            _ptr(y_acc), T, H, K, _ptr(y), _stream(y)))
 
 
 def moe_combine_identity(y_perm, x, slot_row, topk_gate, ffn_scale, y):
     """moe_zero_experts + moe_combine in one pass: y = (sum of the identity
     slots' gates) * x + sum of ffn_scale * gate * y_perm rows, in slot order."""
-    _dev(y_perm, x, slot_row, topk_gate, y)
+    d = _dev(y_perm, x, slot_row, topk_gate, y)
     T, H, K = _combine_args(y_perm, slot_row, topk_gate, y)
     _require(x.shape == (T, H) and x.dtype == y.dtype, "x.shape == (T, H) and x.dtype == y.dtype")
-    _check("moe_combine_identity", lib().moe_combine_identity(
-        _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
-        T, H, K, _ptr(y), _stream(y)))
+    with torch.cuda.device(d):
+        _check("moe_combine_identity", lib().moe_combine_identity(
+            _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
+            T, H, K, _ptr(y), _stream(y)))
 
 
 def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_err):
     """One PID update of the FFN experts' selection bias from a batch's counts."""
-    _dev(counts, bias, integral, prev_err)
+    d = _dev(counts, bias, integral, prev_err)
     _want(counts, torch.int32, "counts")
     for t, n in ((bias, "bias"), (integral, "integral"), (prev_err, "prev_err")):
         _want(t, torch.float32, n)
@@ -329,9 +341,10 @@ def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_e
              "counts.numel() >= n_ffn and bias.numel() >= n_ffn")
     _require(integral.numel() >= n_ffn and prev_err.numel() >= n_ffn,
              "integral.numel() >= n_ffn and prev_err.numel() >= n_ffn")
-    _check("moe_bias_update", lib().moe_bias_update(
-        _ptr(counts), int(T), int(n_ffn), float(target), float(kp), float(ki), float(kd),
-        _ptr(bias), _ptr(integral), _ptr(prev_err), _stream(bias)))
+    with torch.cuda.device(d):
+        _check("moe_bias_update", lib().moe_bias_update(
+            _ptr(counts), int(T), int(n_ffn), float(target), float(kp), float(ki), float(kd),
+            _ptr(bias), _ptr(integral), _ptr(prev_err), _stream(bias)))
 
 
 def moe_router_similarity_workspace_bytes(E, H):
@@ -341,7 +354,7 @@ def moe_router_similarity_workspace_bytes(E, H):
 def moe_router_similarity(w_router, sim, mean, ws):
     """Pairwise cosine similarity of the router's per-expert weight rows into
     sim [E, E] and its off-diagonal mean into mean [1] (fp32 tensors)."""
-    _dev(w_router, sim, mean, ws)
+    d = _dev(w_router, sim, mean, ws)
     _want(w_router, torch.float32, "w_router")
     _want(sim, torch.float32, "sim")
     _want(mean, torch.float32, "mean")
@@ -349,9 +362,10 @@ def moe_router_similarity(w_router, sim, mean, ws):
     _require(sim.shape == (E, E) and mean.numel() >= 1, "sim.shape == (E, E) and mean.numel() >= 1")
     _require(w_router.is_contiguous() and sim.is_contiguous(),
              "w_router.is_contiguous() and sim.is_contiguous()")
-    _check("moe_router_similarity", lib().moe_router_similarity(
-        _ptr(w_router), E, H, _ptr(sim), _ptr(mean), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(w_router)))
+    with torch.cuda.device(d):
+        _check("moe_router_similarity", lib().moe_router_similarity(
+            _ptr(w_router), E, H, _ptr(sim), _ptr(mean), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream(w_router)))
 
 
 # ------------------------------------------------------------ diagnostics --
