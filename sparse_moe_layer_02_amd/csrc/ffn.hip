@@ -1097,24 +1097,47 @@ __global__ __launch_bounds__(kThreads) void ffn_f32(const float* __restrict__ A,
   const size_t wrows = GATEUP ? (size_t)2 * I : (size_t)H;
   const float* wexp = W + (size_t)e * wrows * KD;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // outputs: rows ty*2+{0,1}, cols tx*2+{0,1}
+  // Each thread stages the same tile elements at every K step: column
+  // kk = tid % TK of rows tid / TK + RS j.  Their row addresses (the gather
+  // resolved once) are set up before the loop, and the next step's values
+  // are fetched into registers while the current step is multiplied.
+  constexpr int NA = TM * TK / kThreads, NW = NB * TK / kThreads;
+  static_assert(kThreads % TK == 0 && NA * kThreads == TM * TK && NW * kThreads == NB * TK,
+                "tile elements split evenly over the threads");
+  const int kk = threadIdx.x % TK, r0 = threadIdx.x / TK;
+  constexpr int RS = kThreads / TK;   // rows apart between a thread's elements
+  const float* arow[NA];
+  const float* wrow[NW];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = r0 + RS * j;
+    const int ar = r >= rows ? -1 : gather ? min(max(gather[row0 + r], 0) / gK, gT - 1) : row0 + r;
+    arow[j] = ar < 0 ? nullptr : A + (size_t)ar * KD + kk;
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int c = r0 + RS * j;
+    const int n = n0 + (c % TN);
+    const int wr = (GATEUP && c >= TN) ? I + n : n;
+    wrow[j] = n < NOUT ? wexp + (size_t)wr * KD + kk : nullptr;
+  }
+  float ra[NA], rw[NW];
+  auto fetch = [&](int k0) {
+    const bool kin = k0 + kk < KD;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) ra[j] = (arow[j] && kin) ? arow[j][k0] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) rw[j] = (wrow[j] && kin) ? wrow[j][k0] : 0.0f;
+  };
   float acc[2][2][2] = {};
+  fetch(0);
   for (int k0 = 0; k0 < KD; k0 += TK) {
-    for (int i = threadIdx.x; i < TM * TK; i += kThreads) {
-      const int r = i / TK, k = i % TK;
-      if (r < rows && k0 + k < KD) {
-        const int ar = gather ? min(max(gather[row0 + r], 0) / gK, gT - 1) : row0 + r;
-        As[k][r] = A[(size_t)ar * KD + k0 + k];
-      } else {
-        As[k][r] = 0.0f;
-      }
-    }
-    for (int i = threadIdx.x; i < NB * TK; i += kThreads) {
-      const int c = i / TK, k = i % TK;
-      int n = n0 + (c % TN);
-      int wr = (GATEUP && c >= TN) ? I + n : n;
-      Bs[k][c] = (n < NOUT && k0 + k < KD) ? wexp[(size_t)wr * KD + k0 + k] : 0.0f;
-    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) As[kk][r0 + RS * j] = ra[j];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) Bs[kk][r0 + RS * j] = rw[j];
     __syncthreads();
+    if (k0 + TK < KD) fetch(k0 + TK);
     for (int k = 0; k < TK; ++k) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {

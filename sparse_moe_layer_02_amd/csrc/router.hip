@@ -38,14 +38,33 @@ __global__ __launch_bounds__(kThreads) void router_fma(const TX* __restrict__ x,
   __shared__ float Bs[kTK][kTN + 4];
   const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  // Each thread stages column kk = tid % kTK of rows tid / kTK + RS j of
+  // both tiles at every K step; the next step's values are fetched into
+  // registers while the current step is multiplied.
+  constexpr int NL = kTM * kTK / kThreads, RS = kThreads / kTK;
+  static_assert(kTM == kTN && kThreads % kTK == 0 && NL * kThreads == kTM * kTK,
+                "tile elements split evenly over the threads");
+  const int kk = threadIdx.x % kTK, r0 = threadIdx.x / kTK;
+  float rx[NL], rw[NL];
+  auto fetch = [&](int k0) {
+    const bool kin = k0 + kk < H;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int r = r0 + RS * j;
+      rx[j] = (m0 + r < T && kin) ? ld_f32(x + (size_t)(m0 + r) * H + k0 + kk) : 0.0f;
+      rw[j] = (n0 + r < E && kin) ? w[(size_t)(n0 + r) * H + k0 + kk] : 0.0f;
+    }
+  };
   float acc[4][4] = {};
+  fetch(0);
   for (int k0 = 0; k0 < H; k0 += kTK) {
-    for (int i = threadIdx.x; i < kTM * kTK; i += kThreads) {
-      const int r = i / kTK, k = i % kTK;
-      As[k][r] = (m0 + r < T && k0 + k < H) ? ld_f32(x + (size_t)(m0 + r) * H + k0 + k) : 0.0f;
-      Bs[k][r] = (n0 + r < E && k0 + k < H) ? w[(size_t)(n0 + r) * H + k0 + k] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      As[kk][r0 + RS * j] = rx[j];
+      Bs[kk][r0 + RS * j] = rw[j];
     }
     __syncthreads();
+    if (k0 + kTK < H) fetch(k0 + kTK);
 #pragma unroll
     for (int k = 0; k < kTK; ++k) {
       float a[4], b[4];
