@@ -229,6 +229,38 @@ moe_status moe_combine_identity(const void *y_perm, const void *x, int dtype,
                                 float ffn_scale, int T, int H, int K, void *y,
                                 void *stream);
 
+/* The whole layer in one call (Technical Report notes, Key claims [§2.1]
+ * router over one pool of FFN and zero-computation experts with the
+ * selection bias, [§2.2] dispatch and combine, [§2.3.2] compensation factor
+ * on the FFN outputs, [§2.4] shapes): the five calls of the default path,
+ * enqueued on `stream` in this order with the intermediate tensors in `ws`:
+ *   moe_router_logits_planes (w_planes may be NULL: moe_router_logits),
+ *   moe_route, moe_permute (indices only), moe_expert_ffn_gather with
+ *   rows_cap = T*K, moe_combine_identity.
+ * y is bitwise the y of those five calls.
+ *   x [T][H] (dtype), w_router [E][H] fp32, w_planes [3][E][H] bf16 or NULL,
+ *   bias [E] fp32, w13 [n_ffn][2I][H] and w2 [n_ffn][H][I] (dtype; may be
+ *   NULL when n_ffn == 0), y [T][H] (dtype), dev_status as for moe_route
+ *   (may be NULL).  Expert ids 0..n_ffn-1 are FFN experts, n_ffn..E-1
+ *   identity experts.
+ *   ws: at least moe_forward_workspace_bytes(T, H, E, n_ffn, I, K, dtype)
+ *   bytes, 256-byte aligned, caller-owned; it holds, in order and each
+ *   256-byte aligned, logits [T][E] fp32, topk_idx and topk_gate [T][K],
+ *   counts [E], offsets [n_ffn+1], row_src and slot_row [T*K], y_perm
+ *   [T*K][H] (dtype) and the expert GEMMs' workspace, which the caller may
+ *   read after the call.
+ * Every check of the five calls runs first: MOE_ERR_NULL, MOE_ERR_DTYPE,
+ * MOE_ERR_SHAPE (T, H, E, K, n_ffn, I out of the ranges the five calls take:
+ * H % 8, 1 <= K <= E <= 1024, n_ffn <= E; bf16: H % 128, I % 64),
+ * MOE_ERR_ALIGN (x, y, w_planes 16 bytes; bf16 weights 16 bytes, fp32 ones
+ * 4; ws 256), MOE_ERR_WORKSPACE; a failed check enqueues nothing.
+ * moe_forward_workspace_bytes returns 0 for sizes out of range. */
+size_t moe_forward_workspace_bytes(int T, int H, int E, int n_ffn, int I, int K, int dtype);
+moe_status moe_forward(const void *x, int dtype, const float *w_router, const void *w_planes,
+                       const float *bias, const void *w13, const void *w2, int T, int H, int E,
+                       int n_ffn, int I, int K, float ffn_scale, void *y, int32_t *dev_status,
+                       void *ws, size_t ws_bytes, void *stream);
+
 /* Bias controller (Technical Report notes, Key claims [§2.1.1, §2.1.2] and
  * Method: each FFN expert's selection bias is adjusted from token-routing
  * frequency by a PID controller so that the average number of activated FFN

@@ -47,6 +47,9 @@ _SIGS = {
                          ctypes.c_float, _P, _P, _P, _P], _I),
     "moe_router_similarity_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "moe_router_similarity": ([_P, _I, _I, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "moe_forward_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I], ctypes.c_size_t),
+    "moe_forward": ([_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                     _P, ctypes.c_size_t, _P], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_profile_enable": ([_I], _I),
     "moe_profile_select": ([ctypes.c_char_p], _I),
@@ -329,6 +332,42 @@ def moe_combine_identity(y_perm, x, slot_row, topk_gate, ffn_scale, y):
         _check("moe_combine_identity", lib().moe_combine_identity(
             _ptr(y_perm), _ptr(x), _DT[y.dtype], _ptr(slot_row), _ptr(topk_gate), float(ffn_scale),
             T, H, K, _ptr(y), _stream(y)))
+
+
+def moe_forward_workspace_bytes(T, H, E, n_ffn, I, K, dtype):
+    """Bytes of moe_forward's workspace (0 for sizes out of range)."""
+    return int(lib().moe_forward_workspace_bytes(T, H, E, n_ffn, I, K, _DT[dtype]))
+
+
+def moe_forward(x, w_router, bias, w13, w2, K, ffn_scale, y, ws, w_planes=None, dev_status=None):
+    """The whole layer in one C call: the five calls of forward()'s default
+    path with their intermediate tensors in ws (a uint8 tensor of at least
+    moe_forward_workspace_bytes bytes)."""
+    d = _dev(x, w_router, bias, w13, w2, y, ws, w_planes, dev_status)
+    _want(w_router, torch.float32, "w_router")
+    _want(bias, torch.float32, "bias")
+    _want(ws, torch.uint8, "ws")
+    for t, n in ((w13, "w13"), (w2, "w2"), (y, "y")):
+        _want(t, x.dtype, n)
+    T, H = x.shape
+    E = w_router.shape[0]
+    n_ffn, I = w13.shape[0], w2.shape[2]
+    _require(w_router.shape == (E, H) and bias.shape == (E,) and y.shape == (T, H),
+             "w_router.shape == (E, H) and bias.shape == (E,) and y.shape == (T, H)")
+    _require(w13.shape == (n_ffn, 2 * I, H) and w2.shape == (n_ffn, H, I),
+             "w13.shape == (n_ffn, 2I, H) and w2.shape == (n_ffn, H, I)")
+    if w_planes is not None:
+        _want(w_planes, torch.bfloat16, "w_planes")
+        _require(w_planes.shape == (3, E, H), "w_planes.shape == (3, E, H)")
+    if dev_status is not None:
+        _want(dev_status, torch.int32, "dev_status")
+        _require(dev_status.numel() >= 1, "dev_status.numel() >= 1")
+    with torch.cuda.device(d):
+        _check("moe_forward", lib().moe_forward(
+            _ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(w_planes), _ptr(bias), _ptr(w13),
+            _ptr(w2), T, H, E, n_ffn, I, K, float(ffn_scale), _ptr(y), _ptr(dev_status),
+            _ptr(ws), ws.numel(), _stream(x)))
+    return y
 
 
 def moe_bias_update(counts, T, n_ffn, target, kp, ki, kd, bias, integral, prev_err):

@@ -223,6 +223,101 @@ moe_status moe_bias_update(const int32_t* counts, int T, int n_ffn, float target
                                      prev_err, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------ one-call forward --
+namespace {
+struct ForwardWs {
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_src;
+  int32_t* slot_row;
+  void* y_perm;
+  void* ffn;
+  size_t ffn_bytes;
+  size_t total;
+};
+
+inline size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Parts of moe_forward's workspace, each 256-byte aligned, in this order.
+ForwardWs forward_ws(char* base, int T, int H, int E, int n_ffn, int I, int K, int dtype) {
+  const size_t rows = (size_t)T * K, es = dtype == MOE_BF16 ? 2 : 4;
+  ForwardWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += al256(bytes);
+    return p;
+  };
+  w.logits = (float*)take((size_t)T * E * 4);
+  w.idx = (int32_t*)take(rows * 4);
+  w.gate = (float*)take(rows * 4);
+  w.counts = (int32_t*)take((size_t)E * 4);
+  w.offsets = (int32_t*)take(((size_t)n_ffn + 1) * 4);
+  w.row_src = (int32_t*)take(rows * 4);
+  w.slot_row = (int32_t*)take(rows * 4);
+  w.y_perm = take(rows * H * es);
+  w.ffn_bytes = n_ffn > 0 ? ffn_ws_bytes((int)rows, n_ffn, I, dtype) : 0;
+  w.ffn = take(w.ffn_bytes);
+  w.total = off;
+  return w;
+}
+
+// Every check of the five calls moe_forward makes, before any of them.
+moe_status forward_checks(const void* x, int dtype, const float* w_router, const void* w_planes,
+                          const float* bias, const void* w13, const void* w2, int T, int H, int E,
+                          int n_ffn, int I, int K, const void* y, const int32_t* dev_status,
+                          const void* ws) {
+  if (!x || !w_router || !bias || !y || !ws || (n_ffn > 0 && (!w13 || !w2))) return MOE_ERR_NULL;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (T < 1 || H < 1 || H % 8 || E < 1 || E > kMaxE || K < 1 || K > E || K > kMaxKCombine ||
+      n_ffn < 0 || n_ffn > E || n_ffn > kMaxFfn || I < 1 || !fits_i32((long long)T * K) ||
+      !fits_i32((long long)T * E))
+    return MOE_ERR_SHAPE;
+  if (dtype == MOE_BF16 && (H % 128 || I % 64)) return MOE_ERR_SHAPE;
+  if (dtype == MOE_F32 && (long long)T * K / 32 + n_ffn + 8 > 65535) return MOE_ERR_SHAPE;
+  const size_t al = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(x, 16) || !aligned(w_router, 4) || !aligned(w_planes, 16) || !aligned(bias, 4) ||
+      !aligned(w13, al) || !aligned(w2, al) || !aligned(y, 16) || !aligned(dev_status, 4) ||
+      !aligned(ws, 256))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_forward_workspace_bytes(int T, int H, int E, int n_ffn, int I, int K, int dtype) {
+  if (T < 1 || H < 1 || E < 1 || n_ffn < 0 || n_ffn > E || I < 1 || K < 1 || !dtype_ok(dtype) ||
+      !fits_i32((long long)T * K) || !fits_i32((long long)T * E))
+    return 0;
+  return forward_ws(nullptr, T, H, E, n_ffn, I, K, dtype).total;
+}
+
+moe_status moe_forward(const void* x, int dtype, const float* w_router, const void* w_planes,
+                       const float* bias, const void* w13, const void* w2, int T, int H, int E,
+                       int n_ffn, int I, int K, float ffn_scale, void* y, int32_t* dev_status,
+                       void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = forward_checks(x, dtype, w_router, w_planes, bias, w13, w2, T, H, E,
+                                       n_ffn, I, K, y, dev_status, ws);
+  if (st != MOE_OK) return st;
+  const ForwardWs w = forward_ws((char*)ws, T, H, E, n_ffn, I, K, dtype);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_router_logits(x, dtype, w_router, w_planes, T, H, E, w.logits, s);
+  if (e == hipSuccess)
+    e = launch_route(w.logits, bias, T, E, K, w.idx, w.gate, w.counts, dev_status, s);
+  if (e == hipSuccess)
+    e = launch_permute(x, dtype, w.idx, w.counts, T, H, K, n_ffn, w.offsets, nullptr, w.row_src,
+                       w.slot_row, s);
+  if (e == hipSuccess && n_ffn > 0)
+    e = launch_expert_ffn(x, w.row_src, K, T, w.offsets, T * K, n_ffn, H, I, w13, w2, dtype,
+                          w.y_perm, w.ffn, s);
+  if (e == hipSuccess)
+    e = launch_combine(w.y_perm, dtype, w.slot_row, w.gate, ffn_scale, nullptr, x, T, H, K, y, s);
+  return launched(e);
+}
+
 size_t moe_router_similarity_workspace_bytes(int E, int H) {
   if (E < 1 || H < 1 || H % 4 || !fits_i32((long long)E * E)) return 0;
   return similarity_ws_bytes(E, H);

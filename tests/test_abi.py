@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe._SIGS)
@@ -192,6 +192,42 @@ def test_combine_identity_validation():
     assert f(*a) == ALIGN
     a = list(args); a[9] = P(0x10004)             # y
     assert f(*a) == ALIGN
+
+
+def test_forward_validation():
+    # the one-call forward runs every check of its five calls before any of
+    # them, so a bad argument enqueues nothing (here: no HIP call at all)
+    lib = moe.lib()
+    q = lib.moe_forward_workspace_bytes
+    assert q(8, 128, 24, 16, 64, 4, 1) > 0
+    assert q(0, 128, 24, 16, 64, 4, 1) == 0 and q(8, 128, 24, 30, 64, 4, 1) == 0
+    assert q(8, 128, 24, 16, 64, 4, 7) == 0
+    ws_bytes = q(8, 128, 24, 16, 64, 4, 1)
+    f = lib.moe_forward
+    one = ctypes.c_float(1.0)
+    # x, dtype, w_router, w_planes, bias, w13, w2, T, H, E, n_ffn, I, K, s, y, status, ws, bytes
+    args = [FAKE, 1, FAKE, None, FAKE, FAKE, FAKE, 8, 128, 24, 16, 64, 4, one, FAKE, None, FAKE,
+            ws_bytes, None]
+    for i in (0, 2, 4, 14, 16):                   # x, w_router, bias, y, ws
+        a = list(args); a[i] = None
+        assert f(*a) == NULL, i
+    a = list(args); a[5] = None                   # FFN weights, with FFN experts
+    assert f(*a) == NULL
+    a = list(args); a[10] = 0; a[5] = a[6] = None   # no FFN experts: no weights needed,
+    a[17] = 1                                     # so the workspace is the failing check
+    assert f(*a) == WS
+    a = list(args); a[1] = 4
+    assert f(*a) == DTYPE
+    for i, v in ((7, 0), (8, 100), (8, 64), (9, 2000), (12, 0), (12, 25), (10, 25), (11, 32)):
+        a = list(args); a[i] = v                  # T, H % 8, bf16 H % 128, E, K, K > E, n_ffn > E, I % 64
+        assert f(*a) == SHAPE, (i, v)
+    for i in (0, 3, 14):                          # x, w_planes, y: 16 bytes
+        a = list(args); a[i] = P(0x10008)
+        assert f(*a) == ALIGN, i
+    a = list(args); a[16] = P(0x10080)            # ws: 256 bytes
+    assert f(*a) == ALIGN
+    a = list(args); a[17] = ws_bytes - 1
+    assert f(*a) == WS
 
 
 def test_binding_rejects_host_tensors():
