@@ -68,3 +68,45 @@ def test_one_call_matches_the_five_calls(name, over, heavy, planes):
                                   host(y), host(idx))
     print(f"end-to-end normwise {err:.3e}, flipped tokens {flips}", flush=True)
     assert err <= TOL[cfg.dtype]
+
+
+def test_one_call_captured_replays_match_eager():
+    # moe_forward allocates nothing and sets no memory with hipMemset: captured
+    # into a HIP graph (torch.cuda.CUDAGraph) it must give on every replay,
+    # from a poisoned workspace and output, bit for bit the eager y
+    dev = device()
+    cfg = workload.CONFIGS["mid_bf16"].replace(T=1024)
+    print(f"\n[case] graph capture of moe_forward {cfg.name} T={cfg.T}", flush=True)
+    inp = workload.make_inputs(cfg, dev)
+    nbytes = moe.moe_forward_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.N, cfg.I, cfg.K,
+                                             cfg.torch_dtype)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    y = torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device=dev)
+
+    def run():
+        moe.moe_forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K,
+                        cfg.scale, y, ws)
+
+    run()
+    torch.cuda.synchronize(dev)
+    ref = y.clone()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize(dev)
+    other = torch.randn(1 << 20, device=dev)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0xAB)
+        other.mul_(1.0001)
+        torch.cuda.synchronize(dev)
+        graph.replay()
+        other.add_(1.0)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(y, ref), f"replay {rep}"
